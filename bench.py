@@ -1,0 +1,309 @@
+"""Benchmark: draft-tree steps/s of the DFlash + DDTree kernel chain on one GPU.
+
+One step = one pass of the whole chain over one batch of synthetic input:
+  1. drafter-mode attention  (16 block queries over 2048 context + 16 own
+     rows, 32 q-heads / 8 KV heads, head_dim 128, bf16)
+  2. log-softmax + top-32    (16 positions x 151936 vocab, fp32)
+  3. tree build              (budget 256, 32 ranks per position)
+  4. verify-mode attention   (257 tree rows over 2048 prefix rows + own
+     rows under the ancestor mask, 32/8/128, bf16)
+  5. acceptance walk + KV compaction (1 layer)
+Inputs: R seeded synthetic sets (the workload's shapes and distributions),
+rotated so that the timed steps read cold HBM rather than the 256 MB
+last-level cache.  All inputs are resident in device memory before timing.
+
+Prints ONE JSON line.  Per-stage device times come from HIP events recorded
+on the launch stream inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "draft-tree steps/s at L=16,B=256,ctx 2048; logit GB/s + attn % MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--sets", type=int, default=20, help="rotated input sets (>= 512 MB total)")
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="time budget of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, msg):
+    if not args.quiet:
+        print(msg, file=sys.stderr, flush=True)
+
+
+class Step:
+    """Device buffers for one input set plus the preallocated outputs."""
+
+    def __init__(self, case, dev, torch, ddt):
+        cfg = case.cfg
+        self.cfg = cfg
+        L, N, ctx = cfg.L, cfg.B + 1, cfg.drafter_ctx
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+
+        self.logits = torch.from_numpy(case.logits).to(dev)
+        self.root = torch.from_numpy(case.root_token).to(dev)
+        self.dq, self.dk, self.dv = bf16(case.dq_bits), bf16(case.dk_bits), bf16(case.dv_bits)
+        self.d_base = torch.zeros(1, dtype=torch.int64, device=dev)
+        self.d_prefix = torch.full((1,), ctx, dtype=torch.int32, device=dev)
+        self.d_nq = torch.full((1,), L, dtype=torch.int32, device=dev)
+        self.vq, self.vk, self.vv = bf16(case.vq_bits), bf16(case.vk_bits), bf16(case.vv_bits)
+        self.kv_base = torch.from_numpy(case.kv_base).to(dev)
+        self.prefix = torch.from_numpy(case.prefix_len).to(dev)
+        self.kc = self.vk[None]          # one layer, compacted in place
+        self.vc = self.vv[None]
+        self.d_out = torch.empty_like(self.dq)
+        self.v_out = torch.empty_like(self.vq)
+        self.ids = torch.empty(L, cfg.K, dtype=torch.int32, device=dev)
+        self.logp = torch.empty(L, cfg.K, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(L, dtype=torch.float32, device=dev)
+        W = (N + 63) // 64
+        self.tree = {
+            "n_nodes": torch.empty(1, dtype=torch.int32, device=dev),
+            "token": torch.empty(1, N, dtype=torch.int32, device=dev),
+            "parent": torch.empty(1, N, dtype=torch.int32, device=dev),
+            "depth": torch.empty(1, N, dtype=torch.int32, device=dev),
+            "score": torch.empty(1, N, dtype=torch.float32, device=dev),
+            "mask": torch.empty(1, N, W, dtype=torch.int64, device=dev),
+        }
+        self.acc = {
+            "accept_len": torch.empty(1, dtype=torch.int32, device=dev),
+            "accepted": torch.empty(1, L + 1, dtype=torch.int32, device=dev),
+            "bonus": torch.empty(1, dtype=torch.int32, device=dev),
+            "new_len": torch.empty(1, dtype=torch.int32, device=dev),
+        }
+        self.target = None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the chain's "
+              "multi-GPU sharding is a design note, not a runnable path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from block_diffusion_draft_vocab_amd import ddt
+
+    ddt.load()
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[3]
+    L, N, K, B = cfg.L, cfg.B + 1, cfg.K, cfg.B
+    ctx, P = cfg.drafter_ctx, cfg.prefix[0]
+    log(args, f"generating {args.sets} input sets")
+    cases = [synth.make_case(cfg, seed=args.seed + 1000 * i) for i in range(args.sets)]
+    steps = [Step(c, dev, torch, ddt) for c in cases]
+
+    d_desc = ddt.attn_desc(1, cfg.hq, cfg.hkv, cfg.D, L, ctx + L)
+    v_desc = ddt.attn_desc(1, cfg.hq, cfg.hkv, cfg.D, N, P + N, (N + 63) // 64)
+    ws_attn_d = torch.empty(max(1, ddt.attention_workspace_size(d_desc)), dtype=torch.uint8,
+                            device=dev)
+    ws_attn_v = torch.empty(max(1, ddt.attention_workspace_size(v_desc)), dtype=torch.uint8,
+                            device=dev)
+    ws_topk = torch.empty(ddt.topk_workspace_size(L, cfg.vocab, K), dtype=torch.uint8,
+                          device=dev)
+
+    def stage_calls(s: Step):
+        return [
+            lambda: ddt.masked_attention(s.dq, s.dk, s.dv, s.d_base, s.d_prefix, s.d_nq, None,
+                                         max_kv_len=ctx + L, out=s.d_out, workspace=ws_attn_d),
+            lambda: ddt.topk_logprobs(s.logits, K, 1.0, ids=s.ids, logp=s.logp, lse=s.lse,
+                                      workspace=ws_topk),
+            lambda: ddt.build_tree(s.logp, s.ids, s.root, 1, L, cfg.k_tree, B, out=s.tree),
+            lambda: ddt.masked_attention(s.vq, s.vk, s.vv, s.kv_base, s.prefix,
+                                         s.tree["n_nodes"], s.tree["mask"], max_kv_len=P + N,
+                                         out=s.v_out, workspace=ws_attn_v),
+            lambda: ddt.accept_compact(s.tree["token"], s.tree["parent"], s.tree["n_nodes"],
+                                       s.target, L, s.kc, s.vc, s.kv_base, s.prefix,
+                                       out=s.acc),
+        ]
+
+    # synthetic target "argmax" per set, along the tree this chain builds
+    depths = []
+    for s, c in zip(steps, cases):
+        for f in stage_calls(s)[:3]:
+            f()
+        torch.cuda.synchronize()
+        tok = s.tree["token"].cpu().numpy()[0]
+        par = s.tree["parent"].cpu().numpy()[0]
+        dep = s.tree["depth"].cpu().numpy()[0]
+        n = int(s.tree["n_nodes"].item())
+        y = synth.sample_target_path(c)[0]
+        s.target = torch.from_numpy(
+            synth.target_for_tree(tok, par, dep, n, y, c.off_path[0])[None]).to(dev)
+        depths.append(dep[:n].astype(np.int64))
+    calls = [stage_calls(s) for s in steps]
+    names = ["drafter_attn", "topk", "tree", "verify_attn", "accept"]
+
+    log(args, f"warmup {args.warmup}")
+    for i in range(args.warmup):
+        for f in calls[i % len(calls)]:
+            f()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(args.steps)]
+    log(args, f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        c = calls[i % len(calls)]
+        e = ev[i]
+        e[0].record(stream)
+        for j, f in enumerate(c):
+            f()
+            e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = np.zeros(len(names))
+    for e in ev:
+        for j in range(len(names)):
+            stage_ms[j] += e[j].elapsed_time(e[j + 1])
+    stage_ms /= args.steps
+    steps_per_s = 1e3 / ms_per_step
+
+    # algorithmic work
+    logit_bytes = L * cfg.vocab * 4 + L * K * 8 + L * 4
+    flops = []
+    for dep in depths:
+        vis = P + (dep + 1)                       # prefix + ancestors incl. self
+        flops.append(4.0 * cfg.D * cfg.hq * float(vis.sum()))
+    verify_flops = float(np.mean(flops))
+    drafter_bytes = ((ctx + L) * cfg.hkv * cfg.D * 2 * 2) + 2 * (L * cfg.hq * cfg.D * 2)
+    t_logit = stage_ms[1] * 1e-3
+    t_verify = stage_ms[3] * 1e-3
+    t_draft = stage_ms[0] * 1e-3
+    logit_gbs = logit_bytes / t_logit / 1e9
+    verify_tflops = verify_flops / t_verify / 1e12
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "verify_attn_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tr = json.load(f)
+        src = os.path.join(ROOT, "block_diffusion_draft_vocab_amd", "csrc", "attention.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if tr.get("source_sha256") == sha:
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "ddtree_step_c3: L=16 V=151936 K=32 B=256 k_tree=32; drafter 16q over "
+                        "2048+16 rows; verify 257q over 2048+257 rows; hq=32 hkv=8 D=128; "
+                        "1 layer compaction",
+            "batch": 1, "input_sets": args.sets,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "verify attention (attn_kernel<128,split> + attn_combine_kernel<128>)",
+            "achieved": round(verify_tflops, 3),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(verify_tflops / BF16_PEAK_TFLOPS, 5),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": verify_flops,
+        },
+        "stages_us": {n: round(float(m) * 1e3, 3) for n, m in zip(names, stage_ms)},
+        "logit_pass": {
+            "bound": "hbm", "achieved": round(logit_gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(logit_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": logit_bytes,
+        },
+        "drafter_attn": {
+            "bound": "hbm", "achieved": round(drafter_bytes / t_draft / 1e9, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(drafter_bytes / t_draft / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": drafter_bytes,
+        },
+    }
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(cases[0], args.cpu_seconds, args)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(case, budget_s, args):
+    """The oracle, as it stands, running the same chain step on the host."""
+    import synth
+    from oracle.accept import accept_compact
+    from oracle.attention import masked_attention
+    from oracle.logits import topk_logprobs
+    from oracle.tree import build_trees
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    cfg = case.cfg
+    L, N, ctx = cfg.L, cfg.B + 1, cfg.drafter_ctx
+    dq = synth.bf16_bits_to_f32(case.dq_bits)
+    dk = synth.bf16_bits_to_f32(case.dk_bits)
+    dv = synth.bf16_bits_to_f32(case.dv_bits)
+    vq = synth.bf16_bits_to_f32(case.vq_bits)
+    vk = synth.bf16_bits_to_f32(case.vk_bits)
+    vv = synth.bf16_bits_to_f32(case.vv_bits)
+    y = synth.sample_target_path(case)
+    n_steps = 0
+    t0 = time.perf_counter()
+    while True:
+        masked_attention(dq, dk, dv, [0], [ctx], [L], None)
+        ids, logp, _ = topk_logprobs(case.logits, cfg.K)
+        t = build_trees(logp, ids, case.root_token, 1, L, cfg.k_tree, cfg.B)
+        masked_attention(vq, vk, vv, case.kv_base, case.prefix_len, t["n_nodes"], t["mask"])
+        tgt = synth.target_for_tree(t["token"][0], t["parent"][0], t["depth"][0],
+                                    int(t["n_nodes"][0]), y[0], case.off_path[0])[None]
+        accept_compact(t["token"], t["parent"], t["n_nodes"], tgt, L, case.vk_bits[None],
+                       case.vv_bits[None], case.kv_base, case.prefix_len)
+        n_steps += 1
+        el = time.perf_counter() - t0
+        log(args, f"cpu baseline step {n_steps}: {el:.1f}s")
+        if el >= budget_s:
+            break
+    return {"value": round(n_steps / el, 4), "unit": "steps/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n_steps} full oracle chain steps on input set 0 ({el:.1f} s of host "
+                      f"time; float64 numpy, BLAS threads={cores})"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+// Stage 4: greedy acceptance walk + KV-cache compaction.
+//
+// [DDTree] "방법론 자세히 보기" (method in detail): the verifier walks the
+// tree along the target's outputs, accepts the longest matching path and
+// removes the rejected branches from the KV cache.
+//
+// One workgroup per (request, layer).  Every workgroup redoes the walk (a
+// few hundred integer compares), so layers are compacted in parallel with no
+// inter-workgroup communication:
+//   next[p] = the child c of p whose token equals target[p] (sibling tokens
+//             are distinct, so each p has at most one such child and the
+//             write is race-free)
+//   the path follows next[] from the root (at most L steps).
+// Compaction moves rows P + path[j] -> P + j.  A destination row can be the
+// source of a later path entry, so each pass loads every source segment of
+// a column range into registers, waits at a barrier, and only then stores.
+#include "common.h"
+#include "launch.h"
+
+namespace ddt {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+constexpr int kAcceptThreads = 256;
+constexpr int kRegs = 8;
+
+__global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
+    const int32_t* __restrict__ token, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ n_nodes, int n_max, const int32_t* __restrict__ target, int L,
+    uint16_t* k_cache, uint16_t* v_cache, const int64_t* __restrict__ kv_base,
+    const int32_t* __restrict__ prefix_len, int n_layers, int64_t layer_stride, int row_elems,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ accepted,
+    int32_t* __restrict__ bonus, int32_t* __restrict__ new_len) {
+  extern __shared__ int sh[];
+  int* next = sh;            // [n_max]
+  int* path = sh + n_max;    // [L + 1]
+  int* misc = path + L + 1;  // [2]
+  const int r = blockIdx.x;
+  const int layer = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t nb = (int64_t)r * n_max;
+  int n = n_nodes[r];
+  n = n < 1 ? 1 : (n > n_max ? n_max : n);
+
+  for (int i = tid; i < n_max; i += kAcceptThreads) next[i] = -1;
+  __syncthreads();
+  for (int c = 1 + tid; c < n; c += kAcceptThreads) {
+    const int p = parent[nb + c];
+    if (p >= 0 && p < n && token[nb + c] == target[nb + p]) next[p] = c;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int cur = 0, len = 0;
+    path[0] = 0;
+    while (len < L) {
+      const int nx = next[cur];
+      if (nx < 0) break;
+      path[++len] = nx;
+      cur = nx;
+    }
+    misc[0] = len;
+    misc[1] = target[nb + cur];
+  }
+  __syncthreads();
+  const int len = misc[0];
+  const int P = prefix_len[r];
+  if (layer == 0) {
+    for (int j = tid; j <= L; j += kAcceptThreads)
+      accepted[(int64_t)r * (L + 1) + j] = j <= len ? path[j] : -1;
+    if (tid == 0) {
+      accept_len[r] = len;
+      bonus[r] = misc[1];
+      new_len[r] = P + len + 1;
+    }
+  }
+  if (layer >= n_layers || len == 0) return;
+
+  const int nch = row_elems / 8;  // 16-byte segments per row
+  const int64_t row0 = kv_base[r] + P;
+  const int per_round = kAcceptThreads * kRegs;
+  int cols = per_round / (2 * len);
+  cols = cols < 1 ? 1 : cols;
+  for (int c0 = 0; c0 < nch; c0 += cols) {
+    const int cw = min(cols, nch - c0);
+    const int per_tensor = len * cw;
+    const int items = 2 * per_tensor;
+    u32x4 regs[kRegs];
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) {
+      const int it = tid + i * kAcceptThreads;
+      if (it < items) {
+        const int tsel = it / per_tensor;
+        const int rem = it - tsel * per_tensor;
+        const int j = rem / cw + 1;
+        const int c = c0 + (rem - (j - 1) * cw);
+        const uint16_t* base = (tsel == 0 ? k_cache : v_cache) + layer * layer_stride;
+        regs[i] = *reinterpret_cast<const u32x4*>(base + (row0 + path[j]) * row_elems + c * 8);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kRegs; ++i) {
+      const int it = tid + i * kAcceptThreads;
+      if (it < items) {
+        const int tsel = it / per_tensor;
+        const int rem = it - tsel * per_tensor;
+        const int j = rem / cw + 1;
+        const int c = c0 + (rem - (j - 1) * cw);
+        if (path[j] != j) {
+          uint16_t* base = (tsel == 0 ? k_cache : v_cache) + layer * layer_stride;
+          *reinterpret_cast<u32x4*>(base + (row0 + j) * row_elems + c * 8) = regs[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_accept(const int32_t* token, const int32_t* parent, const int32_t* n_nodes,
+                         int n_max, const int32_t* target, int batch, int L, void* k_cache,
+                         void* v_cache, const int64_t* kv_base, const int32_t* prefix_len,
+                         int n_layers, int64_t layer_stride, int hkv, int head_dim,
+                         int32_t* accept_len, int32_t* accepted, int32_t* bonus,
+                         int32_t* new_len, hipStream_t stream) {
+  const size_t smem = (size_t)(n_max + L + 1 + 2) * sizeof(int);
+  const int layers = n_layers > 0 ? n_layers : 1;
+  hipLaunchKernelGGL(accept_kernel, dim3(batch, layers), dim3(kAcceptThreads), smem, stream,
+                     token, parent, n_nodes, n_max, target, L,
+                     static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), kv_base,
+                     prefix_len, n_layers, layer_stride, hkv * head_dim, accept_len, accepted,
+                     bonus, new_len);
+  return hipGetLastError();
+}
+
+}  // namespace ddt

@@ -1,0 +1,56 @@
+// Host-side launchers of the libddt kernels (internal; the public ABI is
+// include/ddt.h).  Arguments are validated by the ABI layer before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ddt {
+
+// ---- stage 1 --------------------------------------------------------------
+struct TopkPlan {
+  int n_chunks;
+  int chunk_len;  // multiple of 4, <= kTopkMaxChunk
+};
+constexpr int kTopkThreads = 256;
+constexpr int kTopkPerThread = 32;
+constexpr int kTopkMaxChunk = kTopkThreads * kTopkPerThread;  // 8192
+TopkPlan topk_plan(int n_rows, int vocab, int k);
+bool topk_supported(int n_rows, int vocab, int k);
+size_t topk_workspace_bytes(int n_rows, int vocab, int k);
+hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, int k,
+                       float inv_t, int32_t* ids, float* logp, float* lse, void* ws,
+                       hipStream_t stream);
+
+// ---- stage 2 --------------------------------------------------------------
+size_t tree_smem_bytes(int L, int k_tree, int budget);
+hipError_t launch_tree(const float* logp, const int32_t* ids, const int32_t* root, int batch,
+                       int L, int k, int k_tree, int budget, int32_t* n_nodes,
+                       int32_t* token, int32_t* parent, int32_t* depth, float* score,
+                       uint64_t* mask, hipStream_t stream);
+
+// ---- stage 3 --------------------------------------------------------------
+struct AttnPlan {
+  int n_cg;             // column groups per (request, kv head)
+  int n_split;          // key splits
+  int tiles_per_split;  // 32-key tiles per split
+};
+AttnPlan attn_plan(int batch, int hq, int hkv, int n_q_max, int max_kv_len);
+size_t attn_workspace_bytes(int batch, int hq, int hkv, int head_dim, int n_q_max,
+                            int max_kv_len);
+hipError_t launch_attention(int batch, int hq, int hkv, int head_dim, int n_q_max,
+                            int mask_words, int max_kv_len, float scale, const void* q,
+                            const void* k, const void* v, const int64_t* kv_base,
+                            const int32_t* prefix_len, const int32_t* n_q,
+                            const uint64_t* mask, void* out, float* lse, void* ws,
+                            hipStream_t stream);
+
+// ---- stage 4 --------------------------------------------------------------
+hipError_t launch_accept(const int32_t* token, const int32_t* parent, const int32_t* n_nodes,
+                         int n_max, const int32_t* target, int batch, int L, void* k_cache,
+                         void* v_cache, const int64_t* kv_base, const int32_t* prefix_len,
+                         int n_layers, int64_t layer_stride, int hkv, int head_dim,
+                         int32_t* accept_len, int32_t* accepted, int32_t* bonus,
+                         int32_t* new_len, hipStream_t stream);
+
+}  // namespace ddt

@@ -1,0 +1,132 @@
+"""C-ABI checks that run without a GPU: the built library loads, exports
+every function include/ddt.h declares, and rejects bad arguments with the
+documented status code before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_draft_vocab_amd import ddt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ddt.h")
+FAKE = ctypes.c_void_p(256)      # non-null, 16-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ddt.lib_path()):
+        pytest.fail("libddt.so is not built (python -m block_diffusion_draft_vocab_amd.build)")
+    return ddt.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ddt_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 9
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(ddt.SIGNATURES)
+    assert lib.ddt_abi_version() == 1
+    assert lib.ddt_status_string(0) == b"ok"
+
+
+def _topk(lib, logits=FAKE, ld=1000, rows=4, V=1000, k=4, inv_t=1.0, ids=FAKE, logp=FAKE,
+          ws=FAKE, wsb=1 << 30):
+    return lib.ddt_topk_logprobs(logits, ld, rows, V, k, inv_t, ids, logp, None, ws, wsb, None)
+
+
+def test_topk_validation(lib):
+    E = ddt
+    assert _topk(lib, logits=None) == E.DDT_EINVAL
+    assert _topk(lib, ids=None) == E.DDT_EINVAL
+    assert _topk(lib, k=1001) == E.DDT_EINVAL
+    assert _topk(lib, k=129) == E.DDT_EINVAL
+    assert _topk(lib, k=0) == E.DDT_EINVAL
+    assert _topk(lib, rows=0) == E.DDT_EINVAL
+    assert _topk(lib, ld=999) == E.DDT_EINVAL
+    assert _topk(lib, inv_t=0.0) == E.DDT_EINVAL
+    assert _topk(lib, inv_t=float("inf")) == E.DDT_EINVAL
+    assert _topk(lib, ws=None) == E.DDT_EWORKSPACE
+    need = lib.ddt_topk_logprobs_workspace_size(4, 1000, 4)
+    assert need > 0
+    assert _topk(lib, wsb=need - 1) == E.DDT_EWORKSPACE
+    assert lib.ddt_topk_logprobs_workspace_size(4, 1000, 2000) == 0
+
+
+def _tree(lib, batch=1, L=16, k=32, k_tree=32, B=256, logp=FAKE, mask=FAKE):
+    return lib.ddt_build_tree(logp, FAKE, FAKE, batch, L, k, k_tree, B, FAKE, FAKE, FAKE, FAKE,
+                              None, mask, None, 0, None)
+
+
+def test_tree_validation(lib):
+    E = ddt
+    assert _tree(lib, logp=None) == E.DDT_EINVAL
+    assert _tree(lib, mask=None) == E.DDT_EINVAL
+    assert _tree(lib, k_tree=33) == E.DDT_EINVAL
+    assert _tree(lib, k=200, k_tree=129) == E.DDT_EINVAL
+    assert _tree(lib, B=2048) == E.DDT_EINVAL
+    assert _tree(lib, B=-1) == E.DDT_EINVAL
+    assert _tree(lib, L=33) == E.DDT_EINVAL
+    assert _tree(lib, L=0) == E.DDT_EINVAL
+    assert _tree(lib, batch=0) == E.DDT_EINVAL
+    # the largest budgets with wide rows do not fit the LDS selection buffer
+    assert _tree(lib, L=32, k=128, k_tree=128, B=2047) == E.DDT_EUNSUPPORTED
+    assert lib.ddt_build_tree_workspace_size(1, 16, 32, 256) == 0
+
+
+def _attn(lib, desc, q=FAKE, mask=FAKE, ws=FAKE, wsb=1 << 30):
+    return lib.ddt_masked_attention(ctypes.byref(desc), q, FAKE, FAKE, FAKE, FAKE, FAKE, mask,
+                                    FAKE, None, ws, wsb, None)
+
+
+def test_attention_validation(lib):
+    E = ddt
+    good = dict(batch=1, hq=32, hkv=8, head_dim=128, n_q_max=257, max_kv_len=2305,
+                mask_words=5, scale=0.0)
+
+    def d(**kw):
+        a = dict(good)
+        a.update(kw)
+        return ddt.attn_desc(a["batch"], a["hq"], a["hkv"], a["head_dim"], a["n_q_max"],
+                             a["max_kv_len"], a["mask_words"], a["scale"])
+
+    assert _attn(lib, d(hq=30)) == E.DDT_EINVAL
+    assert _attn(lib, d(head_dim=96)) == E.DDT_EUNSUPPORTED
+    assert _attn(lib, d(head_dim=256)) == E.DDT_EUNSUPPORTED
+    assert _attn(lib, d(mask_words=4)) == E.DDT_EINVAL
+    assert _attn(lib, d(batch=0)) == E.DDT_EINVAL
+    assert _attn(lib, d(max_kv_len=0)) == E.DDT_EINVAL
+    assert _attn(lib, d(), q=None) == E.DDT_EINVAL
+    assert _attn(lib, d(), q=ctypes.c_void_p(258)) == E.DDT_EINVAL     # misaligned
+    assert _attn(lib, d(), ws=None) == E.DDT_EWORKSPACE
+    need = lib.ddt_masked_attention_workspace_size(ctypes.byref(d()))
+    assert need > 0
+    assert _attn(lib, d(), wsb=need - 1) == E.DDT_EWORKSPACE
+    assert lib.ddt_masked_attention_workspace_size(ctypes.byref(d(hq=30))) == 0
+    assert lib.ddt_masked_attention(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                    FAKE, 0, None) == E.DDT_EINVAL
+
+
+def _accept(lib, batch=1, n_max=257, L=16, n_layers=1, hkv=8, D=128, tok=FAKE, kc=FAKE,
+            stride=1 << 20):
+    return lib.ddt_accept_compact(tok, FAKE, FAKE, n_max, FAKE, batch, L, kc, FAKE, FAKE, FAKE,
+                                  n_layers, stride, hkv, D, FAKE, FAKE, FAKE, FAKE, None)
+
+
+def test_accept_validation(lib):
+    E = ddt
+    assert _accept(lib, tok=None) == E.DDT_EINVAL
+    assert _accept(lib, batch=0) == E.DDT_EINVAL
+    assert _accept(lib, L=0) == E.DDT_EINVAL
+    assert _accept(lib, n_layers=-1) == E.DDT_EINVAL
+    assert _accept(lib, hkv=1, D=12) == E.DDT_EINVAL
+    assert _accept(lib, kc=None) == E.DDT_EINVAL
+    assert _accept(lib, kc=ctypes.c_void_p(264)) == E.DDT_EINVAL
+    assert _accept(lib, stride=12) == E.DDT_EINVAL

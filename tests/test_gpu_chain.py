@@ -1,0 +1,111 @@
+"""GPU chain parity: every stage fed by the previous GPU stage, compared at
+the end with the oracle's own chain on the same seeded inputs.
+
+drafter attention -> top-K -> tree -> verify attention -> accept/compact.
+At the tiny config and in the deep regime the GPU tree equals the oracle
+tree exactly (same top-K ids, log-probs within 1e-5 and no boundary tie), so
+the committed tokens, new lengths and compacted caches must match bit for
+bit and the attention outputs within 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from block_diffusion_draft_vocab_amd import ddt
+from oracle.accept import accept_compact as oracle_accept
+from oracle.attention import masked_attention as oracle_attn
+from oracle.logits import topk_logprobs as oracle_topk
+from oracle.tree import build_trees as oracle_trees
+from tests.helpers import bf16_f32, dev_bf16, host_bf16_bits, mask_to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_chain(gpu, cfg, case):
+    b, L, N = cfg.batch, cfg.L, cfg.B + 1
+    # drafter pass
+    ctx = cfg.drafter_ctx
+    dkv_base = torch.arange(b, dtype=torch.int64, device=gpu) * (ctx + L)
+    dout = ddt.masked_attention(dev_bf16(case.dq_bits, gpu), dev_bf16(case.dk_bits, gpu),
+                                dev_bf16(case.dv_bits, gpu), dkv_base,
+                                torch.full((b,), ctx, dtype=torch.int32, device=gpu),
+                                torch.full((b,), L, dtype=torch.int32, device=gpu), None,
+                                max_kv_len=ctx + L)
+    # logit pass + tree
+    ids, logp, _ = ddt.topk_logprobs(torch.from_numpy(case.logits).to(gpu), cfg.K,
+                                     cfg.inv_temperature)
+    tree = ddt.build_tree(logp, ids, torch.from_numpy(case.root_token).to(gpu), b, L,
+                          cfg.k_tree, cfg.B)
+    # verify pass over the tree's own rows
+    kv_base = torch.from_numpy(case.kv_base).to(gpu)
+    prefix = torch.from_numpy(case.prefix_len).to(gpu)
+    k1 = dev_bf16(case.vk_bits, gpu)
+    v1 = dev_bf16(case.vv_bits, gpu)
+    vout = ddt.masked_attention(dev_bf16(case.vq_bits, gpu), k1, v1, kv_base, prefix,
+                                tree["n_nodes"], tree["mask"],
+                                max_kv_len=int(case.prefix_len.max()) + N)
+    torch.cuda.synchronize()
+    tok = tree["token"].cpu().numpy()
+    par = tree["parent"].cpu().numpy()
+    dep = tree["depth"].cpu().numpy()
+    nn = tree["n_nodes"].cpu().numpy()
+    y = synth.sample_target_path(case)
+    tgt = np.stack([synth.target_for_tree(tok[r], par[r], dep[r], int(nn[r]), y[r],
+                                          case.off_path[r]) for r in range(b)])
+    kc = k1[None].clone()
+    vc = v1[None].clone()
+    acc = ddt.accept_compact(tree["token"], tree["parent"], tree["n_nodes"],
+                             torch.from_numpy(tgt).to(gpu), L, kc, vc, kv_base, prefix)
+    torch.cuda.synchronize()
+    return {
+        "drafter": dout.float().cpu().numpy(), "verify": vout.float().cpu().numpy(),
+        "tok": tok, "par": par, "n_nodes": nn, "mask": mask_to_host(tree["mask"]),
+        "accept_len": acc["accept_len"].cpu().numpy(), "accepted": acc["accepted"].cpu().numpy(),
+        "bonus": acc["bonus"].cpu().numpy(), "new_len": acc["new_len"].cpu().numpy(),
+        "k": host_bf16_bits(kc), "v": host_bf16_bits(vc),
+    }
+
+
+def _oracle_chain(cfg, case):
+    b, L, N = cfg.batch, cfg.L, cfg.B + 1
+    ctx = cfg.drafter_ctx
+    dkv_base = np.arange(b, dtype=np.int64) * (ctx + L)
+    dout, _ = oracle_attn(bf16_f32(case.dq_bits), bf16_f32(case.dk_bits), bf16_f32(case.dv_bits),
+                          dkv_base, np.full(b, ctx), np.full(b, L), None)
+    ids, logp, _ = oracle_topk(case.logits, cfg.K, cfg.inv_temperature)
+    t = oracle_trees(logp, ids, case.root_token, b, L, cfg.k_tree, cfg.B)
+    vout, _ = oracle_attn(bf16_f32(case.vq_bits), bf16_f32(case.vk_bits), bf16_f32(case.vv_bits),
+                          case.kv_base, case.prefix_len, t["n_nodes"], t["mask"])
+    y = synth.sample_target_path(case)
+    tgt = np.stack([synth.target_for_tree(t["token"][r], t["parent"][r], t["depth"][r],
+                                          int(t["n_nodes"][r]), y[r], case.off_path[r])
+                    for r in range(b)])
+    acc, path, bonus, new_len, ko, vo = oracle_accept(
+        t["token"], t["parent"], t["n_nodes"], tgt, L, case.vk_bits[None], case.vv_bits[None],
+        case.kv_base, case.prefix_len)
+    return dout, vout, t, acc, path, bonus, new_len, ko, vo
+
+
+@pytest.mark.parametrize("cfg", [synth.CONFIGS[1], synth.scaled(synth.DEEP, vocab=20000, B=64,
+                                                                 K=8, k_tree=8, prefix=(300, 300),
+                                                                 drafter_ctx=100)],
+                         ids=["c1", "deep_small"])
+def test_chain(gpu, cfg):
+    case = synth.make_case(cfg)
+    g = _gpu_chain(gpu, cfg, case)
+    dout, vout, t, acc, path, bonus, new_len, ko, vo = _oracle_chain(cfg, case)
+    assert np.abs(g["drafter"] - dout).max() <= 2e-2
+    assert np.array_equal(g["tok"], t["token"]) and np.array_equal(g["par"], t["parent"])
+    assert np.array_equal(g["mask"], t["mask"])
+    for r in range(cfg.batch):
+        n = int(t["n_nodes"][r])
+        assert np.abs(g["verify"][r, :n] - vout[r, :n]).max() <= 2e-2
+    assert np.array_equal(g["accept_len"], acc)
+    assert np.array_equal(g["accepted"], path)
+    assert np.array_equal(g["bonus"], bonus)
+    assert np.array_equal(g["new_len"], new_len)
+    for r in range(cfg.batch):
+        lo = int(case.kv_base[r])
+        hi = lo + int(new_len[r])
+        assert np.array_equal(g["k"][:, lo:hi], ko[:, lo:hi])
+        assert np.array_equal(g["v"][:, lo:hi], vo[:, lo:hi])

@@ -1,0 +1,127 @@
+"""GPU parity: ddt_build_tree vs the oracle's best-first heap.
+
+Bar: given the same top-K tables, every output array is bit-identical
+(n_nodes, token, parent, depth, score, ancestor mask).  Chained from the GPU
+top-K, node sets agree except swaps whose scores lie within 1e-5 of the B-th
+boundary.  Cases: all workload configs, the deep regime, the hand-worked
+dyadic example, random tables with forced exact ties, budget 0, short
+trees, k_tree < K, budgets up to 2047."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from block_diffusion_draft_vocab_amd import ddt
+from oracle.logits import topk_logprobs as oracle_topk
+from oracle.tree import build_tree as oracle_tree
+from oracle.tree import build_trees as oracle_trees
+from tests.helpers import mask_to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_tree(gpu, logp, ids, root, batch, L, k_tree, B):
+    out = ddt.build_tree(torch.from_numpy(np.ascontiguousarray(logp, np.float32)).to(gpu),
+                         torch.from_numpy(np.ascontiguousarray(ids, np.int32)).to(gpu),
+                         torch.from_numpy(np.asarray(root, np.int32)).to(gpu),
+                         batch, L, k_tree, B)
+    torch.cuda.synchronize()
+    res = {k: v.cpu().numpy() for k, v in out.items() if v is not None}
+    res["mask"] = mask_to_host(out["mask"])
+    return res
+
+
+def _assert_same(g, o):
+    assert np.array_equal(g["n_nodes"], o["n_nodes"])
+    for key in ("token", "parent", "depth"):
+        assert np.array_equal(g[key], o[key]), key
+    assert np.array_equal(g["score"].view(np.uint32), o["score"].view(np.uint32))
+    assert np.array_equal(g["mask"], o["mask"])
+
+
+def _check(gpu, logp, ids, root, batch, L, k_tree, B):
+    g = _gpu_tree(gpu, logp, ids, root, batch, L, k_tree, B)
+    o = oracle_trees(logp, ids, np.asarray(root), batch, L, k_tree, B)
+    _assert_same(g, o)
+    return g
+
+
+@pytest.mark.parametrize("cfg", [synth.CONFIGS[1], synth.CONFIGS[2], synth.CONFIGS[3],
+                                 synth.CONFIGS[4], synth.FLAT4, synth.DEEP, synth.CONFIGS[5]],
+                         ids=["c1", "c2", "c3", "c4", "c4flat", "deep", "c5"])
+def test_tree_workloads(gpu, cfg):
+    case = synth.make_case(cfg, with_drafter=False, with_verify=False)
+    ids, logp, _ = oracle_topk(case.logits, cfg.K, cfg.inv_temperature)
+    g = _check(gpu, logp, ids, case.root_token, cfg.batch, cfg.L, cfg.k_tree, cfg.B)
+    assert np.all(g["n_nodes"] == cfg.B + 1)
+
+
+def test_tree_golden_dyadic(gpu):
+    with open(os.path.join(os.path.dirname(__file__), "golden", "dyadic_tree.json")) as f:
+        gd = json.load(f)
+    inp, exp = gd["inputs"], gd["expected"]
+    logp = np.array([[math.log(p) for p in row] for row in inp["probs"]], dtype=np.float32)
+    ids = np.array(inp["ids"], dtype=np.int32)
+    g = _gpu_tree(gpu, logp, ids, [inp["root_token"]], 1, 2, inp["k_tree"], inp["budget"])
+    assert g["token"][0].tolist() == exp["token"]
+    assert g["parent"][0].tolist() == exp["parent"]
+    assert g["depth"][0].tolist() == exp["depth"]
+    assert [int(w) for w in g["mask"][0, :, 0]] == exp["mask_word0"]
+
+
+def _random_tables(seed, batch, L, K, ties):
+    rng = np.random.default_rng(seed)
+    logp = np.stack([np.sort(np.log(rng.dirichlet(np.ones(2 * K))[:K]))[::-1]
+                     for _ in range(batch * L)]).astype(np.float32)
+    if ties:
+        logp[:, 1::3] = logp[:, 0::3][:, :logp[:, 1::3].shape[1]]
+        logp = -np.sort(-logp, axis=1)
+        logp = np.round(logp * 4) / 4                 # many equal sums
+        logp = np.minimum(logp, 0).astype(np.float32)
+        logp = -np.sort(-logp, axis=1)
+    ids = np.stack([rng.choice(5000, K, replace=False) for _ in range(batch * L)]).astype(np.int32)
+    root = rng.integers(0, 5000, batch).astype(np.int32)
+    return logp, ids, root
+
+
+@pytest.mark.parametrize("seed,batch,L,K,k_tree,B,ties", [
+    (0, 3, 4, 6, 6, 40, False), (1, 2, 8, 16, 9, 300, True), (2, 1, 16, 32, 32, 1024, True),
+    (3, 4, 5, 3, 3, 2047, False), (4, 2, 32, 4, 2, 700, True), (5, 1, 3, 2, 2, 100, False),
+    (6, 2, 10, 128, 128, 512, False), (7, 5, 16, 8, 1, 16, False), (8, 2, 16, 64, 64, 0, False),
+    (9, 1, 1, 64, 64, 64, True)])
+def test_tree_random_tables(gpu, seed, batch, L, K, k_tree, B, ties):
+    logp, ids, root = _random_tables(seed, batch, L, K, ties)
+    _check(gpu, logp, ids, root, batch, L, k_tree, B)
+
+
+def test_tree_chained_from_gpu_topk(gpu):
+    """GPU top-K -> GPU tree vs oracle top-K -> oracle tree: same node set
+    except swaps at the B-th boundary (workload tolerance 1e-5)."""
+    for cfg in (synth.CONFIGS[3], synth.DEEP):
+        case = synth.make_case(cfg, with_drafter=False, with_verify=False)
+        gids, glogp, _ = ddt.topk_logprobs(torch.from_numpy(case.logits).to(gpu), cfg.K)
+        g = _gpu_tree(gpu, glogp.cpu().numpy(), gids.cpu().numpy(), case.root_token, 1,
+                      cfg.L, cfg.k_tree, cfg.B)
+        oids, ologp, _ = oracle_topk(case.logits, cfg.K)
+        o = oracle_tree(ologp, oids, int(case.root_token[0]), cfg.k_tree, cfg.B)
+
+        def paths(t, n):
+            out = {}
+            for s in range(1, n):
+                p, seq = s, []
+                while p > 0:
+                    seq.append(int(t["token"][p]))
+                    p = int(t["parent"][p])
+                out[tuple(reversed(seq))] = float(t["score"][s])
+            return out
+
+        gp = paths({k: v[0] for k, v in g.items()}, int(g["n_nodes"][0]))
+        op = paths(o, o["n_nodes"])
+        boundary = min(op.values())
+        for path in set(gp) ^ set(op):
+            sc = op.get(path, gp.get(path))
+            assert abs(sc - boundary) <= 1e-5
