@@ -12,8 +12,10 @@ Inputs: R seeded synthetic sets (the workload's shapes and distributions),
 rotated so that the timed steps read cold HBM rather than the 256 MB
 last-level cache.  All inputs are resident in device memory before timing.
 
-Prints ONE JSON line.  Per-stage device times come from HIP events recorded
-on the launch stream inside the timed region.
+Prints ONE JSON line.  The step rate comes from replaying one HIP graph per
+input set (every stage of a step in one graph).  Per-stage device times come
+from a second timed region: one graph per stage holding that stage for every
+input set, replayed between HIP events recorded on the launch stream.
 """
 from __future__ import annotations
 
@@ -44,6 +46,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every stage from Python instead of replaying one HIP graph "
+                         "per input set")
     ap.add_argument("--quiet", action="store_true")
     return ap.parse_args()
 
@@ -161,33 +166,85 @@ def main():
     calls = [stage_calls(s) for s in steps]
     names = ["drafter_attn", "topk", "tree", "verify_attn", "accept"]
 
-    log(args, f"warmup {args.warmup}")
-    for i in range(args.warmup):
-        for f in calls[i % len(calls)]:
-            f()
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-          for _ in range(args.steps)]
-    log(args, f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        c = calls[i % len(calls)]
-        e = ev[i]
-        e[0].record(stream)
-        for j, f in enumerate(c):
-            f()
-            e[j + 1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if args.eager:
+        log(args, f"warmup {args.warmup}")
+        for i in range(args.warmup):
+            for f in calls[i % len(calls)]:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(args.steps)]
+        log(args, f"timing {args.steps} eager steps")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            e = ev[i]
+            e[0].record(stream)
+            for j, f in enumerate(calls[i % len(calls)]):
+                f()
+                e[j + 1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        # region A: one HIP graph per input set holds the whole step
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for c in calls:
+                for f in c:
+                    f()
+        torch.cuda.synchronize()
+
+        def capture(fns):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for f in fns:
+                    f()
+            return g
+
+        graphs = [capture(c) for c in calls]
+        log(args, f"warmup {args.warmup}")
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        log(args, f"timing {args.steps} graph steps")
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        # region B: per-stage device time.  One graph per stage holds that
+        # stage for every input set back to back; HIP events on the launch
+        # stream bracket each replay (events cannot be timed inside a
+        # captured graph here), so a launch's average duration includes the
+        # small gap between kernels of one graph.
+        stage_graphs = [capture([c[j] for c in calls]) for j in range(len(names))]
+        reps = max(1, min(args.steps, 1000) // len(calls))
+        ev = []
+        for j, g in enumerate(stage_graphs):
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                g.replay()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        log(args, f"timed {reps} replays of {len(calls)} launches per stage")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     stage_ms = np.zeros(len(names))
-    for e in ev:
-        for j in range(len(names)):
-            stage_ms[j] += e[j].elapsed_time(e[j + 1])
-    stage_ms /= args.steps
+    if args.eager:
+        for e in ev:
+            for j in range(len(names)):
+                stage_ms[j] += e[j].elapsed_time(e[j + 1])
+        stage_ms /= len(ev)
+    else:
+        for j, (a, b) in enumerate(ev):
+            stage_ms[j] = a.elapsed_time(b) / (reps * len(calls))
     steps_per_s = 1e3 / ms_per_step
 
     # algorithmic work
@@ -227,6 +284,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "launch": "eager" if args.eager else "hip_graph_per_step",
         "config": {
             "workload": "ddtree_step_c3: L=16 V=151936 K=32 B=256 k_tree=32; drafter 16q over "
                         "2048+16 rows; verify 257q over 2048+257 rows; hq=32 hkv=8 D=128; "

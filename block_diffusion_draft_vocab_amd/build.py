@@ -26,6 +26,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     # packed fp32 VALU ops stay off: plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in the unified VGPR file, so the softmax rescale of
+    # the attention accumulators needs no AGPR<->VGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE,
 ]
 

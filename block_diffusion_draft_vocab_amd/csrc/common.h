@@ -96,4 +96,132 @@ __device__ inline int block_scan_array(int* arr, int n, int* scratch) {
   return total;
 }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)x, m, kWave);
+  const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Descending bitonic sort of 64*R keys held by one wavefront, R per lane;
+// element i lives in lane i/R, register i%R.  No LDS, no barriers.
+template <int R>
+__device__ inline void wave_sort_desc(uint64_t (&x)[R]) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int k = 2; k <= kWave * R; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int i = lane * R + r;
+          const uint64_t y = shfl_xor_u64(x[r], j / R);
+          const bool take_max = ((i & j) == 0) == ((i & k) == 0);
+          x[r] = take_max ? (x[r] > y ? x[r] : y) : (x[r] < y ? x[r] : y);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (r & j) continue;
+          const int i = lane * R + r;
+          const uint64_t a = x[r], b = x[r | j];
+          const bool desc = (i & k) == 0;
+          const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+          x[r] = desc ? hi : lo;
+          x[r | j] = desc ? lo : hi;
+        }
+      }
+    }
+  }
+}
+
+// One bitonic stage (k, j) on keys held R per lane, element index
+// i = base + lane*R + r; j < 64*R, so partners live in the same wave.
+template <int R>
+__device__ __forceinline__ void bitonic_stage_in_wave(uint64_t (&x)[R], int base, int k, int j) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (j >= R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = base + lane * R + r;
+      const uint64_t y = shfl_xor_u64(x[r], j / R);
+      const bool take_max = ((i & j) == 0) == ((i & k) == 0);
+      x[r] = take_max ? (x[r] > y ? x[r] : y) : (x[r] < y ? x[r] : y);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r & j) continue;
+      const int i = base + lane * R + r;
+      const uint64_t a = x[r], b = x[r | j];
+      const bool desc = (i & k) == 0;
+      const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+      x[r] = desc ? hi : lo;
+      x[r | j] = desc ? lo : hi;
+    }
+  }
+}
+
+// Descending bitonic sort of n keys in LDS (n a power of two, n = W*64*R
+// for the first W waves of the block).  Keys stay in registers; only
+// stages whose partner is in another wave go through LDS (two barriers
+// each).  Every thread of the block calls it; ends with a barrier.
+template <int R>
+__device__ void block_sort_desc_r(uint64_t* a, int n) {
+  const int wid = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int span = kWave * R;
+  const bool active = wid * span < n;
+  const int base = wid * span;
+  uint64_t x[R];
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] = a[base + lane * R + r];
+  }
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= span) {
+        __syncthreads();
+        if (active) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) a[base + lane * R + r] = x[r];
+        }
+        __syncthreads();
+        if (active) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int i = base + lane * R + r;
+            const uint64_t y = a[i ^ j];
+            const bool take_max = ((i & j) == 0) == ((i & k) == 0);
+            x[r] = take_max ? (x[r] > y ? x[r] : y) : (x[r] < y ? x[r] : y);
+          }
+        }
+      } else if (active) {
+        bitonic_stage_in_wave<R>(x, base, k, j);
+      }
+    }
+  }
+  __syncthreads();
+  if (active) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) a[base + lane * R + r] = x[r];
+  }
+  __syncthreads();
+}
+
+// Dispatch: 4 keys per lane where possible (fewer waves, fewer cross-wave
+// stages); sizes beyond 4 keys per lane of every wave use the LDS network.
+__device__ inline void block_sort_desc(uint64_t* a, int n) {
+  const int nw = blockDim.x / kWave;
+  int waves = n / (kWave * 4);
+  waves = waves < 1 ? 1 : (waves > nw ? nw : waves);
+  const int R = n / (kWave * waves);
+  switch (R) {
+    case 1: block_sort_desc_r<1>(a, n); break;
+    case 2: block_sort_desc_r<2>(a, n); break;
+    case 4: block_sort_desc_r<4>(a, n); break;
+    default: bitonic_sort_desc(a, n); break;
+  }
+}
+
 }  // namespace ddt

@@ -12,8 +12,12 @@
 //   G := the depth-1 candidates (already sorted), theta := B-th key of G
 //   for depth d = 2..L:
 //     parents := depth-(d-1) members of G, in G order (index j)
-//     children (j, rank) with key > theta and (j+1)(rank+1) <= B
-//     G := top B of (G u children) by one bitonic sort; theta := G[B-1]
+//     children (j, rank) with key > theta and (j+1)(rank+1) <= B; the
+//       children of one parent form a descending run
+//     G := top B of (G u runs): each key's rank is found by counting the
+//       greater keys of every run (binary search where a run straddles it),
+//       and the keys ranked below B are scattered to their rank
+//     theta := G[B-1]
 //
 // Why it is exact: a node's key is below its parent's and its elder
 // sibling's, so the top-B set is closed under "parent" and "elder sibling";
@@ -50,7 +54,7 @@ __device__ __forceinline__ float key_score(uint64_t key) {
 }
 
 struct TreeLayout {
-  int sort_cap;
+  int cand_cap;   // G plus every candidate a level can produce
   size_t bytes;
 };
 
@@ -66,12 +70,13 @@ static int nc_bound(int B, int k_tree) {
 }
 
 static TreeLayout tree_layout(int L, int k_tree, int B) {
-  int cap = 2;
-  const long need = (long)B + nc_bound(B, k_tree);
-  while (cap < need) cap <<= 1;
   const int Bp = B > 0 ? B : 1;
-  size_t bytes = (size_t)cap * 8 + (size_t)L * k_tree * 4 + (size_t)Bp * 4 * 3 +
-                 (size_t)(Bp + 1) * 4 + 34 * 4 * 2 + 18 * 4 + 4 * 4;
+  const int cap = Bp + nc_bound(B, k_tree);
+  size_t bytes = (size_t)cap * 8 * 2        // keys + merge buffer
+                 + (size_t)L * k_tree * 4   // log-prob table
+                 + (size_t)Bp * 4 * 3       // parent scores, counts, slots
+                 + (size_t)(Bp + 2) * 4 * 3 // run offsets x2, parent slots
+                 + 64 * 34 * 4 + 34 * 4 * 2 + 32 * 4;
   return {cap, bytes};
 }
 
@@ -81,27 +86,38 @@ size_t tree_smem_bytes(int L, int k_tree, int budget) {
 
 namespace {
 
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = threadIdx.x & (kWave - 1);
+  return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+}
+
 __global__ __launch_bounds__(1024) void tree_kernel(
     const float* __restrict__ logp, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ root_token, int L, int K, int k_tree, int B, int sort_cap,
+    const int32_t* __restrict__ root_token, int L, int K, int k_tree, int B, int cand_cap,
     int32_t* __restrict__ n_nodes_out, int32_t* __restrict__ tok_out,
     int32_t* __restrict__ par_out, int32_t* __restrict__ dep_out,
     float* __restrict__ score_out, uint64_t* __restrict__ mask_out) {
   extern __shared__ uint64_t smem_u64[];
   const int Bp = B > 0 ? B : 1;
-  uint64_t* keys = smem_u64;
-  float* y = reinterpret_cast<float*>(keys + sort_cap);
-  float* pscore = y + L * k_tree;
-  int* ibuf = reinterpret_cast<int*>(pscore + Bp);
-  int* slot_tab = ibuf + Bp;
-  int* par_slot = slot_tab + Bp;
-  int* dcount = par_slot + Bp + 1;
-  int* doff = dcount + 34;
-  int* scratch = doff + 34;
+  uint64_t* keys = smem_u64;                       // [cand_cap]
+  uint64_t* kbuf = keys + cand_cap;                // [cand_cap] merge ping-pong
+  float* y = reinterpret_cast<float*>(kbuf + cand_cap);  // [L * k_tree]
+  float* pscore = y + L * k_tree;                  // [Bp]
+  int* rcnt = reinterpret_cast<int*>(pscore + Bp); // [Bp]
+  int* slot_tab = rcnt + Bp;                       // [Bp]
+  int* roff = slot_tab + Bp;                       // [Bp + 2] run offsets
+  int* roff2 = roff + Bp + 2;                      // [Bp + 2]
+  int* par_slot = roff2 + Bp + 2;                  // [Bp + 2]
+  int* wcnt = par_slot + Bp + 2;                   // [64 chunks][34 depths]
+  int* dcount = wcnt + 64 * 34;                    // [34]
+  int* doff = dcount + 34;                         // [34]
+  int* misc = doff + 34;                           // [32]
 
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
   const int n_max = B + 1;
   const int W = (n_max + 63) / 64;
 
@@ -116,67 +132,156 @@ __global__ __launch_bounds__(1024) void tree_kernel(
   __syncthreads();
   uint64_t theta = (g == B && B > 0) ? keys[B - 1] : 0ull;
 
-  for (int d = 2; d <= L && g > 0; ++d) {
-    // parents: depth d-1 members of G, numbered in G order
-    for (int q = tid; q < g; q += nt) ibuf[q] = key_depth(keys[q]) == d - 1;
+  // Level-local index of the depth-dd members among G positions [0, g):
+  // one ballot per wave chunk of 64 positions, a prefix over the chunks.
+  // Returns the count; idx_out[q] gets the index of position q (members).
+  auto index_depth = [&](int dd, int* idx_out) -> int {
+    const int nchunk = (g + kWave - 1) / kWave;
+    for (int c = wid; c < nchunk; c += nt / kWave) {
+      const int q = c * kWave + lane;
+      const bool is = q < g && key_depth(keys[q]) == dd;
+      const uint64_t bal = __ballot(is);
+      if (lane == 0) wcnt[c] = __popcll(bal);
+      if (is) idx_out[q] = __popcll(bal & lanemask_lt());
+    }
     __syncthreads();
-    const int n = block_scan_array(ibuf, g, scratch);
+    if (tid < kWave) {  // nchunk <= 32: one wave scans the chunk counts
+      const int t = tid < nchunk ? wcnt[tid] : 0;
+      const int inc = wave_inclusive_scan(t);
+      if (tid < nchunk) wcnt[tid] = inc - t;
+      if (tid == kWave - 1) misc[0] = inc;
+    }
+    __syncthreads();
+    for (int q = tid; q < g; q += nt)
+      if (key_depth(keys[q]) == dd) idx_out[q] += wcnt[q / kWave];
+    const int total = misc[0];
+    __syncthreads();
+    return total;
+  };
+
+  for (int d = 2; d <= L && g > 0; ++d) {
+    // parents: the depth d-1 members of G, numbered in G order
+    const int n = index_depth(d - 1, slot_tab);
     if (n == 0) break;
     for (int q = tid; q < g; q += nt) {
       const uint64_t kq = keys[q];
-      if (key_depth(kq) == d - 1) pscore[ibuf[q]] = key_score(kq);
+      if (key_depth(kq) == d - 1) pscore[slot_tab[q]] = key_score(kq);
     }
+    for (int j = tid; j < n; j += nt) rcnt[j] = 0;
     __syncthreads();
-    // number of children of each parent that can still enter the top B
+    // candidates (j, c): key above theta and (j+1)(c+1) <= B; for one
+    // parent they form a prefix of ranks, so counting them gives the run
     const float* yd = y + (d - 1) * k_tree;
-    for (int j = tid; j < n; j += nt) {
-      const float s = pscore[j];
-      const int cmax = min(k_tree, B / (j + 1));
-      int c = 0;
-      for (; c < cmax; ++c) {
-        const float sc = s + yd[c];
-        if (tkey(sc, d, j, c) <= theta) break;
-      }
-      ibuf[j] = c;
+    const int items = n * k_tree;
+    for (int it = tid; it < items; it += nt) {
+      const int j = it / k_tree;
+      const int c = it - j * k_tree;
+      if ((j + 1) * (c + 1) <= B && tkey(pscore[j] + yd[c], d, j, c) > theta)
+        atomicAdd(&rcnt[j], 1);
     }
     __syncthreads();
-    const int nc = block_scan_array(ibuf, n, scratch);
+    // run layout: run 0 = G at [0, g), run j+1 = children of parent j
+    const int nc = block_scan_array(rcnt, n, misc + 8);   // rcnt -> offsets
     if (nc == 0) break;
-    for (int j = tid; j < n; j += nt) {
-      const int off = ibuf[j];
-      const int cnt = (j + 1 < n ? ibuf[j + 1] : nc) - off;
-      const float s = pscore[j];
-      for (int c = 0; c < cnt; ++c) keys[g + off + c] = tkey(s + yd[c], d, j, c);
+    for (int it = tid; it < items; it += nt) {
+      const int j = it / k_tree;
+      const int c = it - j * k_tree;
+      const int o = rcnt[j];
+      const int len = (j + 1 < n ? rcnt[j + 1] : nc) - o;
+      if (c < len) keys[g + o + c] = tkey(pscore[j] + yd[c], d, j, c);
     }
-    int M = 2;
-    while (M < g + nc) M <<= 1;
-    for (int i = g + nc + tid; i < M; i += nt) keys[i] = 0ull;
+    for (int j = tid; j <= n + 1; j += nt) {
+      // offsets of runs 0..n, and the end
+      roff[j] = j == 0 ? 0 : (j <= n ? g + rcnt[j - 1] : g + nc);
+    }
     __syncthreads();
-    bitonic_sort_desc(keys, M);
-    g = min(B, g + nc);
+    // pairwise merge-path rounds: runs (2i, 2i+1) -> run i, every output
+    // element placed independently by a binary search on its diagonal
+    const int total = g + nc;
+    int R = n + 1;
+    uint64_t* src = keys;
+    uint64_t* dst = kbuf;
+    int* ro = roff;
+    int* ro_next = roff2;
+    while (R > 1) {
+      const int Rn = (R + 1) >> 1;
+      for (int p = tid; p < total; p += nt) {
+        // pair i with ro[2i] <= p < ro[2i+2]
+        int lo = 0, hi = Rn - 1;
+        while (lo < hi) {
+          const int m = (lo + hi + 1) >> 1;
+          if (ro[2 * m] <= p) lo = m; else hi = m - 1;
+        }
+        const int a0 = ro[2 * lo];
+        const int a1 = ro[2 * lo + 1];
+        const int b1 = 2 * lo + 2 <= R ? ro[2 * lo + 2] : a1;
+        const int la = a1 - a0, lb = b1 - a1;
+        const int kk = p - a0;
+        int l2 = kk - lb > 0 ? kk - lb : 0;
+        int h2 = kk < la ? kk : la;
+        while (l2 < h2) {
+          const int m = (l2 + h2) >> 1;
+          if (src[a0 + m] > src[a1 + kk - 1 - m]) l2 = m + 1; else h2 = m;
+        }
+        const int ai = l2, bi = kk - l2;
+        const bool take_a = bi >= lb || (ai < la && src[a0 + ai] > src[a1 + bi]);
+        dst[p] = take_a ? src[a0 + ai] : src[a1 + bi];
+      }
+      for (int i = tid; i <= Rn; i += nt) ro_next[i] = i < Rn ? ro[2 * i] : total;
+      __syncthreads();
+      uint64_t* t = src; src = dst; dst = t;
+      int* u = ro; ro = ro_next; ro_next = u;
+      R = Rn;
+    }
+    g = min(B, total);
+    if (src != keys)
+      for (int i = tid; i < g; i += nt) keys[i] = src[i];
+    __syncthreads();
     theta = (g == B) ? keys[B - 1] : 0ull;
   }
 
   // ---- flatten: slot of every node, parent slots, outputs, ancestor mask
-  if (tid < 34) dcount[tid] = 0;
-  __syncthreads();
-  for (int q = tid; q < g; q += nt) atomicAdd(&dcount[key_depth(keys[q])], 1);
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int dd = 0; dd < 34; ++dd) {
-      doff[dd] = run;
-      run += dcount[dd];
-    }
-  }
-  __syncthreads();
-  for (int dd = 1; dd <= L; ++dd) {
-    if (dcount[dd] == 0) continue;
-    for (int q = tid; q < g; q += nt) ibuf[q] = key_depth(keys[q]) == dd;
+  // level-local index of every node within its depth, all depths at once:
+  // per chunk of 64 positions one ballot per depth, then a prefix per depth
+  {
+    const int nchunk = (g + kWave - 1) / kWave;
+    for (int i = tid; i < nchunk * 34; i += nt) wcnt[i] = 0;
     __syncthreads();
-    block_scan_array(ibuf, g, scratch);
-    for (int q = tid; q < g; q += nt)
-      if (key_depth(keys[q]) == dd) slot_tab[doff[dd] + ibuf[q]] = q + 1;
+    for (int c = wid; c < nchunk; c += nt / kWave) {
+      const int q = c * kWave + lane;
+      const int dq = q < g ? key_depth(keys[q]) : 0;
+      for (int dd = 1; dd <= L; ++dd) {
+        const uint64_t bal = __ballot(dq == dd);
+        if (bal == 0) continue;
+        if (lane == 0) wcnt[c * 34 + dd] = __popcll(bal);
+        if (dq == dd) slot_tab[q] = __popcll(bal & lanemask_lt());
+      }
+    }
+    __syncthreads();
+    if (tid < 34) {
+      const int dd = tid;
+      int run = 0;
+      for (int c = 0; c < nchunk; ++c) {
+        const int t = wcnt[c * 34 + dd];
+        wcnt[c * 34 + dd] = run;
+        run += t;
+      }
+      dcount[dd] = run;
+    }
+    __syncthreads();
+    if (tid < kWave) {
+      const int t = tid < 34 ? dcount[tid] : 0;
+      const int inc = wave_inclusive_scan(t);
+      if (tid < 34) doff[tid] = inc - t;
+    }
+    __syncthreads();
+    for (int q = tid; q < g; q += nt) {
+      const int dq = key_depth(keys[q]);
+      slot_tab[q] = doff[dq] + wcnt[(q / kWave) * 34 + dq] + slot_tab[q];
+    }
+    __syncthreads();
+    // slot_tab[q] = position of node q in the depth-major order; invert it
+    for (int q = tid; q < g; q += nt) roff[slot_tab[q]] = q + 1;
     __syncthreads();
   }
   if (tid == 0) par_slot[0] = -1;
@@ -185,7 +290,7 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     const int dq = key_depth(kq);
     const int pl = key_pr(kq) >> 7;
     const int ti = dq == 1 ? -1 : doff[dq - 1] + pl;
-    par_slot[q + 1] = (ti >= 0 && ti < g) ? slot_tab[ti] : 0;
+    par_slot[q + 1] = (ti >= 0 && ti < g) ? roff[ti] : 0;
   }
   __syncthreads();
 
@@ -241,12 +346,14 @@ hipError_t launch_tree(const float* logp, const int32_t* ids, const int32_t* roo
                        int32_t* token, int32_t* parent, int32_t* depth, float* score,
                        uint64_t* mask, hipStream_t stream) {
   const TreeLayout lay = tree_layout(L, k_tree, budget);
-  const int threads = lay.sort_cap >= 2048 ? 1024 : (lay.sort_cap >= 1024 ? 512 : 256);
+  // enough threads for one merge element per thread at the common sizes
+  int threads = 256;
+  while (threads < 1024 && threads < lay.cand_cap) threads <<= 1;
   if (lay.bytes > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(tree_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
   hipLaunchKernelGGL(tree_kernel, dim3(batch), dim3(threads), lay.bytes, stream, logp, ids,
-                     root, L, k, k_tree, budget, lay.sort_cap, n_nodes, token, parent, depth,
+                     root, L, k, k_tree, budget, lay.cand_cap, n_nodes, token, parent, depth,
                      score, mask);
   return hipGetLastError();
 }
