@@ -50,7 +50,22 @@ def parse():
                     help="launch every stage from Python instead of replaying one HIP graph "
                          "per input set")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run device-to-device copies of MIB MiB (a plain copy kernel of "
+                         "known size, to scale HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_mib": mib, "launches": 5, "bytes_read_per_launch": n * 4,
+                      "bytes_written_per_launch": n * 4}))
 
 
 def log(args, msg):
@@ -106,6 +121,9 @@ class Step:
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the chain's "
               "multi-GPU sharding is a design note, not a runnable path.", file=sys.stderr)
