@@ -95,7 +95,7 @@ DDT_EXPORT int ddt_build_tree(const float* topk_logp, const int32_t* topk_ids,
 static int attn_desc_check(const ddt_attn_desc* d, bool with_mask) {
   if (d == nullptr) return DDT_EINVAL;
   if (d->batch < 1 || d->hq < 1 || d->hkv < 1 || d->hq % d->hkv != 0 || d->n_q_max < 1 ||
-      d->max_kv_len < 1)
+      d->max_kv_len < 1 || d->max_kv_len > (1 << 22))
     return DDT_EINVAL;
   if (with_mask && d->mask_words < (d->n_q_max + 63) / 64) return DDT_EINVAL;
   if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128) return DDT_EUNSUPPORTED;

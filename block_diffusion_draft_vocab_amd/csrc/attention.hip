@@ -9,22 +9,30 @@
 // Work decomposition
 //   A "column" is one (query row, q-head) pair of a KV head; the g = hq/hkv
 //   q-heads of one query are adjacent columns, so they share K/V tiles and
-//   mask bits.  A wave owns 64 columns (two 32-column MFMA blocks), a
-//   workgroup of 4 waves owns 256 columns and one range of 32-key tiles.
-//   Grid x = (column group, request, KV head) with the KV head fastest, so
-//   with 8 KV heads every workgroup of one head lands on the same XCD and
-//   its K/V tiles stay in that XCD's L2.  Grid y = key split; a second
+//   mask bits.  A workgroup has 8 waves (two per SIMD, so one wave's softmax
+//   overlaps the other's MFMAs); wave w owns the 32 columns [32w, 32w+32) of
+//   the workgroup's 256 and every wave walks the same 64-key tiles.
+//   The 1-D grid enumerates (KV head, request, column group, key split) with
+//   the KV head fastest: workgroups are dealt to the 8 XCDs round-robin, so
+//   with 8 KV heads all workgroups of one head share an XCD and its L2.  A
+//   trailing column group with few columns gets fewer key splits.  A second
 //   kernel merges the splits with their log-sum-exp weights.
 //
-// Per 32-key tile (staged once in LDS for the 4 waves):
-//   S^T (keys x cols) = K (32 x D) . Q^T        v_mfma_f32_32x32x16_bf16
-//   each lane then holds 16 keys of ONE column, so the softmax row
-//   reductions need only one exchange with lane^32;
-//   O^T (D x cols) += V^T (D x 32) . P^T        P taken straight from the
-//   S^T registers (keys relabelled inside each 16-key chunk; V is written
-//   to LDS transposed with the same relabelling).
-// Visibility is applied per key from a 32-bit window of the column's mask
-// row; tiles no column of a wave can see are skipped.
+// Per 64-key tile
+//   staging: K and V rows are copied global -> LDS by the load unit itself
+//     (global_load_lds_dwordx4, no registers involved), the 16-byte chunks
+//     of each row XOR-swizzled by (row & 7) against bank conflicts; a ring
+//     of three tiles keeps the copies two tiles ahead, one barrier per tile.
+//   S^T (keys x cols) = K . Q^T     v_mfma_f32_32x32x16_bf16, two 32-key
+//     halves = two independent accumulation chains.  Each lane then holds 16
+//     keys of ONE column per half, so a row reduction needs one exchange
+//     with lane^32 (v_permlane32_swap).
+//   O^T (D x cols) += V^T . P^T     P straight from the S^T registers (keys
+//     relabelled inside each 16-key chunk), V^T fragments read from the
+//     row-major V tile with the transposing ds_read_b64_tr_b16.
+// Visibility is applied per key from a 64-bit window of the column's mask
+// row, computed for all own-row tiles of the split before the tile loop and
+// kept in LDS; tiles no column of the workgroup can see are skipped.
 #include <math.h>
 
 #include "common.h"
@@ -34,23 +42,33 @@ namespace ddt {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+#define LDS_AS __attribute__((address_space(3)))
 
-constexpr int kKT = 32;
+constexpr int kKT = 64;  // keys per tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kColsPerWave = 32;
 constexpr int kColsPerWG = kWaves * kColsPerWave;
+constexpr int kRing = 3;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;
-constexpr int kMaxTilesPerSplit = 32;
+constexpr int kMaxTilesPerSplit = 16;
+constexpr int kCUs = 256;
 
 template <int D>
-struct Smem {
-  uint16_t k[kKT][D + 8];   // row-major, padded against bank conflicts
-  uint16_t vt[D][kKT + 8];  // transposed, keys relabelled per 16-chunk
+struct Geo {
+  static constexpr int kCh = D / 8;                        // 16-byte chunks per key row
+  static constexpr int kSwz = kCh < 8 ? kCh - 1 : 7;       // chunk XOR mask
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kKT * kRowBytes;       // one K or V tile
+  static constexpr int kLoads = 2 * kKT * kCh / kThreads;  // 16-byte copies per thread per tile
+  static constexpr int kSmem = 2 * kRing * kTileBytes;     // K ring, then V ring
 };
 
 struct Params {
@@ -63,76 +81,178 @@ struct Params {
   const uint64_t* mask;
   uint16_t* out;
   float* lse;
-  float* part_o;
-  float2* part_ml;
-  int batch, hq, hkv, n_q_max, mask_words, n_cg, n_split, tps;
+  uint16_t* part_o;   // bf16 [rows][n_split][D], normalised by the split's own sum
+  float2* part_ml;    // [rows][n_split] = (max in log2 units, sum of 2^(x - max))
+  int batch, hq, hkv, n_q_max, mask_words;
+  int n_cg_full;      // column groups with all 8 waves busy at n_q_max
+  int n_split;        // key splits of those groups
+  int n_split_tail;   // key splits of the trailing partial group (0: none)
   float scale_log2;
 };
 
-// Position of key kt (0..31) inside its LDS V^T row: within each 16-key
-// chunk keys {0-3, 8-11} come first, then {4-7, 12-15}.  That is the order
-// in which a 32x32 accumulator half (lanes 0-31 / 32-63) holds them.
-__device__ __forceinline__ int vt_pos(int kt) {
-  const int w = kt & 15;
-  return (kt & ~15) | (w & 3) | ((w & 4) << 1) | ((w & 8) >> 1);
+// Tiles [t0, t1) of split s out of n_split over nt tiles (balanced; 32-bit
+// products: n_split <= 2^15 and nt < 2^16 under the plan's limits).
+__device__ __forceinline__ void split_range(int s, int n_split, int nt, int& t0, int& t1) {
+  t0 = (int)((uint32_t)(s * nt) / (uint32_t)n_split);
+  t1 = (int)((uint32_t)((s + 1) * nt) / (uint32_t)n_split);
+}
+// Split s is empty only when there are fewer tiles than splits.
+__device__ __forceinline__ bool split_nonempty(int s, int n_split, int nt) {
+  if (nt >= n_split) return true;
+  int t0, t1;
+  split_range(s, n_split, nt, t0, t1);
+  return t0 < t1;
 }
 
-// Bits b in [0, 32) = bit (j0 + b) of a little-endian u64 row of W words,
-// zero outside [0, 64 W).  Requires j0 > -32.
-__device__ __forceinline__ uint32_t extract32(const uint64_t* row, int W, int j0) {
-  const int j = j0 < 0 ? 0 : j0;
-  const int w = j >> 6;
-  const int sh = j & 63;
-  const uint64_t lo = w < W ? row[w] : 0ull;
-  const uint64_t hi = (w + 1) < W ? row[w + 1] : 0ull;
-  const uint64_t v = sh ? ((lo >> sh) | (hi << (64 - sh))) : lo;
-  const uint32_t r = (uint32_t)v;
-  return j0 < 0 ? (r << (-j0)) : r;
+// Words j0>>6 and (j0>>6)+1 of a mask row of W words (word 0 and nothing
+// when j0 < 0), zero past the row.
+__device__ __forceinline__ void mask_words_for(const uint64_t* mrow, int W, int j0, uint64_t& lo,
+                                               uint64_t& hi) {
+  const int w = j0 < 0 ? 0 : (j0 >> 6);
+  lo = w < W ? mrow[w] : 0ull;
+  hi = (j0 >= 0 && w + 1 < W) ? mrow[w + 1] : 0ull;
 }
 
-// Which of the 32 keys [key0, key0+32) a column may see.
-__device__ __forceinline__ uint32_t visible_window(int key0, int P, int nq, const uint64_t* mrow,
-                                                   int W, bool valid) {
-  if (!valid) return 0u;
-  if (key0 + kKT <= P) return 0xFFFFFFFFu;
-  const uint32_t pre = key0 >= P ? 0u : ((1u << (P - key0)) - 1u);
+// Which of the 64 keys [key0, key0+64) a column may see: all prefix keys,
+// and own keys j in [0, nq) that its mask row allows (all of them without a
+// mask).  lo/hi come from mask_words_for(key0 - P); key0 + 64 > P - 64.
+__device__ __forceinline__ uint64_t visible64(int key0, int P, int nq, bool has_mask,
+                                              uint64_t lo, uint64_t hi) {
+  if (key0 + kKT <= P) return ~0ull;
+  const uint64_t pre = key0 >= P ? 0ull : ((1ull << (P - key0)) - 1ull);
   const int j0 = key0 - P;
-  const int lo = j0 < 0 ? -j0 : 0;
-  int hi = nq - j0;
-  hi = hi > 32 ? 32 : hi;
-  uint32_t range = 0u;
-  if (hi > lo) range = (hi >= 32 ? 0xFFFFFFFFu : ((1u << hi) - 1u)) & ~((1u << lo) - 1u);
-  const uint32_t own = mrow != nullptr ? extract32(mrow, W, j0) : 0xFFFFFFFFu;
+  const int b_lo = j0 < 0 ? -j0 : 0;
+  int b_hi = nq - j0;
+  b_hi = b_hi > 64 ? 64 : b_hi;
+  uint64_t range = 0ull;
+  if (b_hi > b_lo)
+    range = (b_hi >= 64 ? ~0ull : ((1ull << b_hi) - 1ull)) & ~((1ull << b_lo) - 1ull);
+  uint64_t own = ~0ull;
+  if (has_mask) {
+    const int sh = j0 & 63;
+    own = j0 < 0 ? (lo << (-j0)) : (sh ? ((lo >> sh) | (hi << (64 - sh))) : lo);
+  }
   return pre | (own & range);
 }
 
-__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4*>(p);
+// x combined with the value of lane ^ 32 (same column, other key half).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// 8 waves per workgroup, wave w owns the 32 columns [32w, 32w+32) of the
-// workgroup's 256 and every wave walks the same tiles (two per SIMD, so one
-// wave's softmax overlaps the other's MFMAs).  Tiles sit in a ring of three
-// LDS buffers, loaded two tiles ahead, with one barrier per tile.
+// One ds_read_b64_tr_b16 (issued as inline asm: the compiler's intrinsic
+// makes every use wait for all LDS-direct copies in flight, including the
+// ones for later tiles).  The caller waits on lgkmcnt with lds_wait_all.
+template <int OFF>
+__device__ __forceinline__ i16x4 lds_tr(uint32_t addr) {
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+__device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t a) {
+  return *(const LDS_AS bf16x8*)(uintptr_t)a;
+}
+
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// Wait for every LDS read in flight; the registers of t are tied to the
+// wait so that no use of them can be scheduled above it.
+template <int R>
+__device__ __forceinline__ void lds_wait_all(i16x4 (&t)[R][2]) {
+  if constexpr (R == 1) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0][0]), "+v"(t[0][1]));
+  } else if constexpr (R == 2) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]));
+  } else {
+    static_assert(R == 4, "head_dim");
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]), "+v"(t[2][0]),
+                   "+v"(t[2][1]), "+v"(t[3][0]), "+v"(t[3][1]));
+  }
+}
+
+// Wait until only the newest 2R LDS reads (the next chunk's) are in flight;
+// the registers of t (the older chunk) are tied to the wait.
+template <int R>
+__device__ __forceinline__ void lds_wait_keep(i16x4 (&t)[R][2]) {
+  if constexpr (R == 1) {
+    asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(t[0][0]), "+v"(t[0][1]));
+  } else if constexpr (R == 2) {
+    asm volatile("s_waitcnt lgkmcnt(4)"
+                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]));
+  } else {
+    static_assert(R == 4, "head_dim");
+    asm volatile("s_waitcnt lgkmcnt(8)"
+                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]), "+v"(t[2][0]),
+                   "+v"(t[2][1]), "+v"(t[3][0]), "+v"(t[3][1]));
+  }
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (expcnt / lgkmcnt fields left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0xF70 | N);
+}
+
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  Smem<D>* sm = reinterpret_cast<Smem<D>*>(smem_raw);   // ring of 3 tiles
+  using G = Geo<D>;
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
   __shared__ int tile_list[kMaxTilesPerSplit];
   __shared__ int n_tiles_s;
   __shared__ uint32_t own_need[kMaxTilesPerSplit];
+  __shared__ uint64_t win_lds[kMaxTilesPerSplit][kColsPerWG];  // own-row tile windows
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = tid >> 6;
   const int h2 = lane >> 5;
   const int n = lane & 31;
 
-  const int x = blockIdx.x;
-  const int hk = x % p.hkv;
-  const int rest = x / p.hkv;
-  const int r = rest % p.batch;
-  const int cg = rest / p.batch;
-  const int s = blockIdx.y;
+  // ---- decode the work item
+  int x = blockIdx.x;
+  const int heavy = p.n_cg_full * p.batch * p.hkv * p.n_split;
+  int hk, r, cg, s, n_split;
+  if (x < heavy) {
+    hk = x % p.hkv;
+    x /= p.hkv;
+    r = x % p.batch;
+    x /= p.batch;
+    cg = x % p.n_cg_full;
+    s = x / p.n_cg_full;
+    n_split = p.n_split;
+  } else {
+    x -= heavy;
+    hk = x % p.hkv;
+    x /= p.hkv;
+    r = x % p.batch;
+    s = x / p.batch;
+    cg = p.n_cg_full;
+    n_split = p.n_split_tail;
+  }
 
   const int P = p.prefix_len[r];
   const int nq = min(p.n_q[r], p.n_q_max);
@@ -140,13 +260,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int g = p.hq / p.hkv;
   const int ncols = nq * g;
   const int col0 = cg * kColsPerWG;
-  if (col0 >= ncols) return;
+  if (col0 >= ncols || T <= 0) return;
   const int ntiles = (T + kKT - 1) / kKT;
-  const int t_begin = s * p.tps;
-  const int t_end = min(ntiles, t_begin + p.tps);
+  int t_begin, t_end;
+  split_range(s, n_split, ntiles, t_begin, t_end);
   if (t_begin >= t_end) return;
+  // a split spans at most kMaxTilesPerSplit tiles whenever every request's
+  // prefix_len + n_q is within the max_kv_len the plan was made for; the
+  // clamp only keeps a violated bound from indexing past the tile list
+  if (t_end - t_begin > kMaxTilesPerSplit) t_end = t_begin + kMaxTilesPerSplit;
   const int64_t base = p.kv_base[r];
   const bool wave_active = col0 + wid * kColsPerWave < ncols;
+  const bool has_mask = p.mask != nullptr;
 
   // ---- this lane's column
   const int col = col0 + wid * kColsPerWave + n;
@@ -154,23 +279,86 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int qi = valid ? col / g : 0;
   const int head = hk * g + (valid ? col % g : 0);
   const uint64_t* mrow =
-      p.mask != nullptr ? p.mask + ((int64_t)r * p.n_q_max + qi) * p.mask_words : nullptr;
+      has_mask ? p.mask + ((int64_t)r * p.n_q_max + qi) * p.mask_words : nullptr;
+  const bool lane_mask = has_mask && valid;
+
+  // ---- staging: copy j of this thread moves 16-byte chunk
+  // L = (8 j + wid) * 64 + lane of the (K tile | V tile) pair; a wave's 64
+  // chunks are contiguous in LDS, which is what the LDS-direct load writes.
+  // Copies j < kLoads/2 are K chunks, the rest V (with one copy per thread,
+  // waves 0-3 copy K and waves 4-7 V).
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS void*)smem_raw;
+  const int row_stride = p.hkv * D;  // elements; a request's rows span < 2^31 elements
+  const uint16_t* kbase = p.k + base * row_stride + (int64_t)hk * D;
+  const uint16_t* vbase = p.v + base * row_stride + (int64_t)hk * D;
+  int ld_row[G::kLoads];
+  int ld_col[G::kLoads];       // element offset of the logical chunk
+  uint32_t ld_lds[G::kLoads];  // wave-uniform LDS offset inside one slot pair
+  constexpr int kPer = kKT * G::kCh;
+#pragma unroll
+  for (int j = 0; j < G::kLoads; ++j) {
+    const int L = (8 * j + wid) * 64 + lane;
+    const bool isv = G::kLoads == 1 ? wid >= 4 : j >= G::kLoads / 2;
+    const int Lt = isv ? L - kPer : L;
+    ld_row[j] = Lt / G::kCh;
+    ld_col[j] = ((Lt % G::kCh) ^ (ld_row[j] & G::kSwz)) * 8;
+    ld_lds[j] = (uint32_t)((Lt - lane) * 16) + (isv ? kRing * G::kTileBytes : 0);
+  }
+  auto issue_tile = [&](int t, int slot) {
+    const int key0 = t * kKT;
+    const int last = T - 1 - key0;  // rows past the end copy a valid row, never visible
+#pragma unroll
+    for (int j = 0; j < G::kLoads; ++j) {
+      const bool isv = G::kLoads == 1 ? wid >= 4 : j >= G::kLoads / 2;
+      const uint16_t* tb = (isv ? vbase : kbase) + (int64_t)key0 * row_stride;
+      const int row = ld_row[j] < last ? ld_row[j] : last;
+      const uint16_t* src = tb + (row * row_stride + ld_col[j]);
+      const uint32_t dst = lds0 + slot * G::kTileBytes + ld_lds[j];
+      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)dst, 16, 0, 0);
+    }
+  };
+
+  // Q and, when the split starts inside the prefix, its first two tiles
+  // (always processed) are put in flight before the tile list is built
+  bf16x8 qf[D / 16];
+  {
+    const uint16_t* qp = p.q + (((int64_t)r * p.n_q_max + qi) * p.hq + head) * D;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      qf[t] = valid ? *reinterpret_cast<const bf16x8*>(qp + 16 * t + 8 * h2) : bf16x8{};
+  }
+  const bool early = t_end - t_begin >= 2 && (t_begin + 2) * kKT <= P;
+  if (early) {
+    issue_tile(t_begin, 0);
+    issue_tile(t_begin + 1, 1);
+  }
 
   // ---- tiles to process: every tile holding prefix keys, and the own-row
-  // tiles in which some column of the workgroup sees a key
+  // tiles in which some column of the workgroup sees a key.  The visibility
+  // windows of the range's own-row tiles are computed here once (their mask
+  // words loaded together: one memory latency) and kept in LDS, so the tile
+  // loop issues no memory operation besides the tile copies.
   const int nt_range = t_end - t_begin;
   const bool listed = t_end * kKT > P;
   int ntl = nt_range;
   if (listed) {
     for (int i = tid; i < nt_range; i += kThreads) own_need[i] = 0u;
+    uint64_t wlo[kMaxTilesPerSplit], whi[kMaxTilesPerSplit];
+#pragma unroll
+    for (int i = 0; i < kMaxTilesPerSplit; ++i) {
+      wlo[i] = whi[i] = 0ull;
+      const int key0 = (t_begin + i) * kKT;
+      if (i < nt_range && key0 + kKT > P && lane_mask)
+        mask_words_for(mrow, p.mask_words, key0 - P, wlo[i], whi[i]);
+    }
     __syncthreads();
-    if (wave_active) {
-      for (int i = 0; i < nt_range; ++i) {
-        const int key0 = (t_begin + i) * kKT;
-        if (key0 + kKT <= P) continue;
-        const uint32_t w = visible_window(key0, P, nq, mrow, p.mask_words, valid);
-        if (__ballot(w != 0u) != 0 && lane == 0) atomicOr(&own_need[i], 1u);
-      }
+#pragma unroll
+    for (int i = 0; i < kMaxTilesPerSplit; ++i) {
+      const int key0 = (t_begin + i) * kKT;
+      if (i >= nt_range || key0 + kKT <= P) continue;
+      const uint64_t w = valid ? visible64(key0, P, nq, has_mask, wlo[i], whi[i]) : 0ull;
+      if (h2 == 0) win_lds[i][wid * kColsPerWave + n] = w;
+      if (wave_active && __ballot(w != 0ull) != 0 && lane == 0) atomicOr(&own_need[i], 1u);
     }
     __syncthreads();
     if (tid == 0) {
@@ -186,244 +374,282 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   }
   auto tile_at = [&](int i) { return listed ? tile_list[i] : t_begin + i; };
 
+  // ---- per-lane LDS read offsets inside one slot.
+  // K as the A operand of S^T: row n (+32 for the second half), logical
+  // chunk 2tt + h2, physical chunk (2tt) ^ (h2 ^ (n & swz)).
+  uint32_t koff[D / 16];
+  {
+    const int w = h2 ^ (n & G::kSwz);
+#pragma unroll
+    for (int tt = 0; tt < D / 16; ++tt)
+      koff[tt] = (uint32_t)(n * G::kRowBytes + (((2 * tt) ^ w) * 16));
+  }
+  // V^T through the transposing read: the address lane (q4 = lane/16, e,
+  // rr) names row (q4/2)*4 + e (+8 for the second read of a pair, +16 per
+  // key chunk) and columns 32 dt + 16 (q4 & 1) + 4 rr, whose physical chunk
+  // is (4 dt) ^ z; the read hands lane l column l%32 of 4 rows, which is the
+  // A-operand layout with key slots matching the P^T registers.
+  uint32_t voff[2];
+  {
+    const int q4 = lane >> 4, e = (lane >> 2) & 3, rr = lane & 3;
+    const int row = (q4 >> 1) * 4 + e;
+    const int y = (q4 & 1) * 2 + (rr >> 1);
+    const int z = y ^ (row & G::kSwz);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      voff[u] = (uint32_t)(row * G::kRowBytes + (((4 * u) ^ z) * 16) + (rr & 1) * 8);
+  }
+
   float m_run = -INFINITY;
   float l_run = 0.f;
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
 
-  // ---- cooperative staging.  Thread = (16-byte chunk of D, key pair) with
-  // the key pair fastest, so a transposed V write instruction covers 16
-  // consecutive words of one LDS row.
-  constexpr int kChunks = D / 8;
-  constexpr int kTasks = 16 * kChunks;
-  const bool has_task = tid < kTasks;
-  const int kp = tid & 15;
-  const int dc = (tid >> 4) % kChunks;
-  const int64_t row_stride = (int64_t)p.hkv * D;
-  const uint16_t* kbase = p.k + base * row_stride + (int64_t)hk * D + dc * 8;
-  const uint16_t* vbase = p.v + base * row_stride + (int64_t)hk * D + dc * 8;
-  u32x4 rk0{}, rk1{}, rv0{}, rv1{};
-  auto load_tile = [&](int t) {
-    const int ka = t * kKT + 2 * kp;
-    const int64_t off = (int64_t)ka * row_stride;
-    const u32x4 z{};
-    rk0 = ka < T ? ld16(kbase + off) : z;
-    rv0 = ka < T ? ld16(vbase + off) : z;
-    rk1 = ka + 1 < T ? ld16(kbase + off + row_stride) : z;
-    rv1 = ka + 1 < T ? ld16(vbase + off + row_stride) : z;
-  };
-  auto store_tile = [&](Smem<D>& b) {
-    *reinterpret_cast<u32x4*>(&b.k[2 * kp][dc * 8]) = rk0;
-    *reinterpret_cast<u32x4*>(&b.k[2 * kp + 1][dc * 8]) = rk1;
-    const int pos = vt_pos(2 * kp);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t a = (rv0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      const uint32_t b2 = (rv1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      *reinterpret_cast<uint32_t*>(&b.vt[dc * 8 + e][pos]) = a | (b2 << 16);
-    }
-  };
+  // prologue: everything is waited for before the loop, so inside it the
+  // only memory operations in flight are tile copies and "all but the
+  // newest tile" is a plain vmcnt
+  if (!early) {
+    if (ntl > 0) issue_tile(tile_at(0), 0);
+    if (ntl > 1) issue_tile(tile_at(1), 1);
+  }
+  wait_vm<0>();
 
-  // prologue: the first two tiles' loads and the Q loads are all in flight
-  // together; the ring of three LDS buffers then keeps loads two tiles ahead
-  u32x4 pk0{}, pk1{}, pv0{}, pv1{};
-  if (has_task && ntl > 0) load_tile(tile_at(0));
-  if (has_task && ntl > 1) {
-    pk0 = rk0; pk1 = rk1; pv0 = rv0; pv1 = rv1;
-    load_tile(tile_at(1));
-  }
-  bf16x8 qf[D / 16];
-  {
-    const uint16_t* qp = p.q + (((int64_t)r * p.n_q_max + qi) * p.hq + head) * D;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      qf[t] = valid ? *reinterpret_cast<const bf16x8*>(qp + 16 * t + 8 * h2) : bf16x8{};
-  }
-  if (has_task && ntl > 1) {
-    store_tile(sm[1]);
-    rk0 = pk0; rk1 = pk1; rv0 = pv0; rv1 = pv1;
-  }
-  if (has_task && ntl > 0) store_tile(sm[0]);
-  __syncthreads();
-  if (has_task && ntl > 2) load_tile(tile_at(2));
   for (int i = 0; i < ntl; ++i) {
-    if (wave_active) {
-      const Smem<D>& b = sm[i % 3];
-      const int key0 = tile_at(i) * kKT;
-      // two independent accumulation chains (even / odd head-dim steps)
-      f32x16 sacc = f32x16{}, sacc1 = f32x16{};
+    // this tile's copies done (the next tile's may stay in flight), then
+    // the barrier publishes it and retires the slot read at i - 1
+    if (i + 1 < ntl) wait_vm<G::kLoads>();
+    else wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+    const int ti = tile_at(i);
+    if (i + 2 < ntl) issue_tile(tile_at(i + 2), (i + 2) % kRing);
+    if (!wave_active) continue;
+    const int key0 = ti * kKT;
+
+    const int slot = i % kRing;
+    const uint32_t kb = lds0 + slot * G::kTileBytes;
+    const uint32_t vb = lds0 + (kRing + slot) * G::kTileBytes;
+    // all K fragments of the tile are read up front (32 reads in flight
+    // instead of a read -> wait -> MFMA chain)
+    bf16x8 ka[D / 16], kb2[D / 16];
 #pragma unroll
-      for (int tt = 0; tt < D / 16; tt += 2) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&b.k[n][16 * tt + 8 * h2]);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&b.k[n][16 * tt + 16 + 8 * h2]);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[tt], sacc, 0, 0, 0);
-        sacc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[tt + 1], sacc1, 0, 0, 0);
-      }
-      sacc += sacc1;
-      float xv[16];
-      float tmax = -INFINITY;
-      if (key0 + kKT <= P) {  // tile inside the prefix: every key visible
+    for (int tt = 0; tt < D / 16; ++tt) {
+      ka[tt] = lds_b128(kb + koff[tt]);
+      kb2[tt] = lds_b128(kb + koff[tt] + 32 * G::kRowBytes);
+    }
+    f32x16 sa = f32x16{}, sb = f32x16{};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          xv[v] = sacc[v];
-          tmax = fmaxf(tmax, xv[v]);
-        }
-      } else {
-        const uint32_t win = visible_window(key0, P, nq, mrow, p.mask_words, valid);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kk = (v >> 2) * 8 + h2 * 4 + (v & 3);
-          xv[v] = ((win >> kk) & 1u) ? sacc[v] : -INFINITY;
-          tmax = fmaxf(tmax, xv[v]);
-        }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave)) * p.scale_log2;
-      // Lazy rescaling: the reference max only moves when the tile max
-      // exceeds it by more than 2^8, so p = 2^(x - m) stays <= 256 and the
-      // O/l rescale (a pass over every accumulator) is rare after the first
-      // tile.  O/l does not depend on the reference.
-      const bool grow = tmax > m_run + kRescaleLog2;
-      if (__ballot(grow) != 0) {
-        const float m_new = grow ? tmax : m_run;
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-        m_run = m_new;
-      }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-      float ls = 0.f;
+    for (int tt = 0; tt < D / 16; ++tt) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[tt], qf[tt], sa, 0, 0, 0);
+      sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb2[tt], qf[tt], sb, 0, 0, 0);
+    }
+    // keep the scheduler from sinking the reads back between the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, D / 8, 0);  // the K reads
+    __builtin_amdgcn_sched_group_barrier(0x008, D / 8, 0);  // then the MFMAs
+    float xv[32];
+    if (key0 + kKT <= P) {  // tile inside the prefix: every key visible
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        xv[v] = __builtin_amdgcn_exp2f(fmaf(xv[v], p.scale_log2, neg_m));
-        ls += xv[v];
+        xv[v] = sa[v];
+        xv[16 + v] = sb[v];
       }
-      l_run += ls;
-      bf16x8 pf[2];
+    } else {
+      const uint64_t win = win_lds[ti - t_begin][wid * kColsPerWave + n] >> (4 * h2);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[c][e] = (__bf16)xv[(2 * c + (e >> 2)) * 4 + (e & 3)];
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(&b.vt[dt * 32 + n][16 * c + 8 * h2]);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], o[dt], 0, 0, 0);
-        }
+      for (int v = 0; v < 16; ++v) {
+        const int kk = (v >> 2) * 8 + (v & 3);
+        xv[v] = ((win >> kk) & 1ull) ? sa[v] : -INFINITY;
+        xv[16 + v] = ((win >> (32 + kk)) & 1ull) ? sb[v] : -INFINITY;
       }
     }
-    if (i + 2 < ntl) {
-      if (has_task) store_tile(sm[(i + 2) % 3]);  // buffer last read at i - 1
-      __syncthreads();
-      if (has_task && i + 3 < ntl) load_tile(tile_at(i + 3));
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 32; ++v) tmax = fmaxf(tmax, xv[v]);
+    tmax = xor32_max(tmax) * p.scale_log2;
+    // Lazy rescaling: the reference max only moves when the tile max
+    // exceeds it by more than 2^8, so p = 2^(x - m) stays <= 256 and the
+    // O/l rescale (a pass over every accumulator) is rare after the first
+    // tile.  O/l does not depend on the reference.
+    const bool grow = tmax > m_run + kRescaleLog2;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      m_run = m_new;
     }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pf[c][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(xv[8 * c + e], p.scale_log2, neg_m));
+    }
+    // row sum of the bf16 weights the P.V product actually uses
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float ls = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pf[c][e], pf[c][e + 1]};
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls, false);
+      }
+    }
+    l_run += ls;
+    const uint32_t va0 = vb + voff[0], va1 = vb + voff[1];
+    // V^T fragments of key chunk c (tile rows [16c, 16c+16)); chunk c+1's
+    // reads are issued before chunk c's MFMAs
+    auto read_chunk = [&](auto cc, i16x4 (&t)[D / 32][2]) {
+      constexpr int c = decltype(cc)::value;
+      constexpr int r0 = 16 * c * G::kRowBytes, r1 = r0 + 8 * G::kRowBytes;
+      static_for<D / 32>([&](auto dd) {
+        constexpr int dt = decltype(dd)::value;
+        const uint32_t va = (dt & 1) ? va1 : va0;
+        t[dt][0] = lds_tr<r0 + (dt >> 1) * 128>(va);
+        t[dt][1] = lds_tr<r1 + (dt >> 1) * 128>(va);
+      });
+    };
+    i16x4 tv[2][D / 32][2];
+    read_chunk(IntC<0>{}, tv[0]);
+    static_for<4>([&](auto cc) {
+      constexpr int c = decltype(cc)::value;
+      if constexpr (c < 3) {
+        read_chunk(IntC<c + 1>{}, tv[(c + 1) & 1]);
+        lds_wait_keep<D / 32>(tv[c & 1]);
+      } else {
+        lds_wait_all(tv[c & 1]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(tv[c & 1][dt][0], tv[c & 1][dt][1]),
+                                                        pf[c], o[dt], 0, 0, 0);
+    });
   }
   if (!wave_active) return;
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+  const float l_tot = xor32_sum(l_run);
   if (!valid) return;
   const int64_t rowid = ((int64_t)r * p.n_q_max + qi) * p.hq + head;
-  if constexpr (!SPLIT) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* op = p.out + rowid * D;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  uint16_t* op = SPLIT ? p.part_o + (rowid * p.n_split + s) * D : p.out + rowid * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+  for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = dt * 32 + a * 8 + h2 * 4;
-        uint16_t h[4];
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = dt * 32 + a * 8 + h2 * 4;
+      uint16_t h[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          h[e] = __builtin_bit_cast(uint16_t, (__bf16)(o[dt][a * 4 + e] * inv));
-        uint2 w;
-        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-        *reinterpret_cast<uint2*>(op + d0) = w;
-      }
+      for (int e = 0; e < 4; ++e)
+        h[e] = __builtin_bit_cast(uint16_t, (__bf16)(o[dt][a * 4 + e] * inv));
+      uint2 w;
+      w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+      w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+      *reinterpret_cast<uint2*>(op + d0) = w;
     }
-    if (p.lse != nullptr && h2 == 0)
-      p.lse[rowid] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  } else {
-    const int64_t ro = rowid * p.n_split + s;
-    float* po = p.part_o + ro * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d0 = dt * 32 + a * 8 + h2 * 4;
-        *reinterpret_cast<float4*>(po + d0) = make_float4(
-            o[dt][a * 4 + 0], o[dt][a * 4 + 1], o[dt][a * 4 + 2], o[dt][a * 4 + 3]);
-      }
+  }
+  if (h2 == 0) {
+    if constexpr (SPLIT) {
+      p.part_ml[rowid * p.n_split + s] = make_float2(m_run, l_tot);
+    } else {
+      if (p.lse != nullptr)
+        p.lse[rowid] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     }
-    if (h2 == 0) p.part_ml[ro] = make_float2(m_run, l_tot);
   }
 }
 
-// Merge of the key splits: one group of D/4 threads per (request, query
-// row, q-head), each thread owning 4 consecutive output elements (float4
-// partial loads, 8-byte bf16 stores).
+// Merge of the key splits: one group of D/8 threads per (request, query
+// row, q-head), each thread owning 8 consecutive output elements (16-byte
+// partial loads and stores).  Splits are read 8 at a time with all 16 loads
+// in flight, merged into a running (max, weighted sum) like the tile loop.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
-  constexpr int kTPR = D / 4;
+  constexpr int kTPR = D / 8;
   constexpr int kRPB = 256 / kTPR;
+  constexpr int kBatch = 8;
   const int gid = blockIdx.x * kRPB + threadIdx.x / kTPR;
   const int lane = threadIdx.x % kTPR;
   if (gid >= p.batch * p.n_q_max * p.hq) return;
+  const int head = gid % p.hq;
   const int rq = gid / p.hq;
   const int qi = rq % p.n_q_max;
   const int r = rq / p.n_q_max;
   const int nq = min(p.n_q[r], p.n_q_max);
   if (qi >= nq) return;
   const int T = p.prefix_len[r] + nq;
+  if (T <= 0) return;
+  const int g = p.hq / p.hkv;
+  const int col = qi * g + head % g;
+  const int ns = col / kColsPerWG < p.n_cg_full ? p.n_split : p.n_split_tail;
   const int ntiles = (T + kKT - 1) / kKT;
-  const int ns = min(p.n_split, (ntiles + p.tps - 1) / p.tps);
   const int64_t ro = (int64_t)gid * p.n_split;
   float M = -INFINITY;
-  for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, p.part_ml[ro + sp].x);
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float Lsum = 0.f;
-  if (M != -INFINITY) {
-    for (int sp = 0; sp < ns; ++sp) {
-      const float2 ml = p.part_ml[ro + sp];
-      const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-      Lsum += ml.y * w;
-      const float4 o4 = *reinterpret_cast<const float4*>(p.part_o + (ro + sp) * D + lane * 4);
-      acc.x += o4.x * w;
-      acc.y += o4.y * w;
-      acc.z += o4.z * w;
-      acc.w += o4.w * w;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sp0 = 0; sp0 < ns; sp0 += kBatch) {
+    float2 ml[kBatch];
+    u32x4 raw[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sp = sp0 + u;
+      const bool ok = sp < ns && split_nonempty(sp, ns, ntiles);
+      ml[u] = ok ? p.part_ml[ro + sp] : make_float2(-INFINITY, 0.f);
+      raw[u] = ok ? *reinterpret_cast<const u32x4*>(p.part_o + (ro + sp) * D + lane * 8)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+    float bm = M;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) bm = fmaxf(bm, ml[u].x);
+    if (bm == -INFINITY) continue;
+    const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - bm);
+    Lsum *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= alpha;
+    M = bm;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = ml[u].x == -INFINITY ? 0.f : ml[u].y * __builtin_amdgcn_exp2f(ml[u].x - M);
+      Lsum += w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += w * __uint_as_float(raw[u][e] << 16);
+        acc[2 * e + 1] += w * __uint_as_float(raw[u][e] & 0xFFFF0000u);
+      }
     }
   }
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-  uint2 wv;
-  wv.x = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.x * inv)) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.y * inv)) << 16);
-  wv.y = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.z * inv)) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc.w * inv)) << 16);
-  *reinterpret_cast<uint2*>(p.out + (int64_t)gid * D + lane * 4) = wv;
+  u32x4 wv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    wv[e] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[2 * e] * inv)) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)(acc[2 * e + 1] * inv)) << 16);
+  *reinterpret_cast<u32x4*>(p.out + (int64_t)gid * D + lane * 8) = wv;
   if (lane == 0 && p.lse != nullptr)
     p.lse[gid] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -INFINITY;
 }
 
+bool plan_splits(const AttnPlan& plan) { return plan.n_split > 1 || plan.n_split_tail > 1; }
+
 template <int D>
 hipError_t launch_d(const Params& prm, const AttnPlan& plan, hipStream_t stream) {
-  const dim3 grid(plan.n_cg * prm.batch * prm.hkv, plan.n_split);
-  constexpr size_t smem = 3 * sizeof(Smem<D>);
-  if (plan.n_split > 1) {
+  const int wgs = (plan.n_cg_full * plan.n_split + plan.n_split_tail) * prm.batch * prm.hkv;
+  constexpr size_t smem = Geo<D>::kSmem;
+  if (wgs <= 0) return hipSuccess;
+  if (plan_splits(plan)) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<D, true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    hipLaunchKernelGGL((attn_kernel<D, true>), grid, dim3(kThreads), smem, stream, prm);
+    hipLaunchKernelGGL((attn_kernel<D, true>), dim3(wgs), dim3(kThreads), smem, stream, prm);
     const int rows = prm.batch * prm.n_q_max * prm.hq;
-    const int rpb = 256 / (D / 4);
+    const int rpb = 256 / (D / 8);
     hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0,
                        stream, prm);
   } else {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<D, false>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    hipLaunchKernelGGL((attn_kernel<D, false>), grid, dim3(kThreads), smem, stream, prm);
+    hipLaunchKernelGGL((attn_kernel<D, false>), dim3(wgs), dim3(kThreads), smem, stream, prm);
   }
   return hipGetLastError();
 }
@@ -434,27 +660,47 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 AttnPlan attn_plan(int batch, int hq, int hkv, int n_q_max, int max_kv_len) {
   const int g = hq / hkv;
-  const int n_cg = (n_q_max * g + kColsPerWG - 1) / kColsPerWG;
+  const int cols = n_q_max * g;
+  const int n_cg_full = cols / kColsPerWG;
+  const int tail_waves = (cols % kColsPerWG + kColsPerWave - 1) / kColsPerWave;
   const int max_tiles = (max_kv_len + kKT - 1) / kKT;
-  // one workgroup per CU where the shape allows it (a second partial round
-  // of workgroups would double the time), long prefixes cut to <= 32 tiles
-  const long wgs = (long)batch * hkv * n_cg;
-  int n_split = (int)(256 / wgs);
-  const int by_len = (max_tiles + kMaxTilesPerSplit - 1) / kMaxTilesPerSplit;
-  if (by_len > n_split) n_split = by_len;
-  if (n_split > max_tiles) n_split = max_tiles;
-  if (n_split < 1) n_split = 1;
-  const int tps = (max_tiles + n_split - 1) / n_split;
-  n_split = (max_tiles + tps - 1) / tps;
-  return {n_cg, n_split, tps};
+  const int min_split = (max_tiles + kMaxTilesPerSplit - 1) / kMaxTilesPerSplit;
+  const long heavy = (long)batch * hkv * n_cg_full;
+  const long tail = tail_waves > 0 ? (long)batch * hkv : 0;
+  // One workgroup per CU (the LDS ring holds one): split the full column
+  // groups as far as the CUs allow, the trailing partial group in proportion
+  // to its busy waves (a lone wave runs a tile in about half the time eight
+  // waves take: copies and barriers do not shrink with it).
+  auto clamp_split = [&](long v) {
+    if (v < min_split) v = min_split;
+    if (v > max_tiles) v = max_tiles;
+    return (int)(v < 1 ? 1 : v);
+  };
+  auto tail_split = [&](int s) {
+    if (tail_waves == 0) return 0;
+    const int t = (s * tail_waves + 1) / 2;
+    return clamp_split(t > s ? s : t);
+  };
+  AttnPlan plan;
+  plan.n_cg_full = n_cg_full;
+  if (heavy > 0) {
+    long s = kCUs / heavy;
+    while (s > 1 && heavy * s + tail * tail_split((int)s) > kCUs) --s;
+    plan.n_split = clamp_split(s);
+    plan.n_split_tail = tail_split(plan.n_split);
+  } else {
+    plan.n_split = clamp_split(kCUs / (tail > 0 ? tail : 1));
+    plan.n_split_tail = tail_waves > 0 ? plan.n_split : 0;
+  }
+  return plan;
 }
 
 size_t attn_workspace_bytes(int batch, int hq, int hkv, int head_dim, int n_q_max,
                             int max_kv_len) {
   const AttnPlan plan = attn_plan(batch, hq, hkv, n_q_max, max_kv_len);
-  if (plan.n_split <= 1) return 0;
+  if (!plan_splits(plan)) return 0;
   const size_t rows = (size_t)batch * n_q_max * hq * plan.n_split;
-  return align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float2));
+  return align256(rows * head_dim * sizeof(uint16_t)) + align256(rows * sizeof(float2));
 }
 
 hipError_t launch_attention(int batch, int hq, int hkv, int head_dim, int n_q_max,
@@ -474,20 +720,20 @@ hipError_t launch_attention(int batch, int hq, int hkv, int head_dim, int n_q_ma
   prm.mask = mask;
   prm.out = static_cast<uint16_t*>(out);
   prm.lse = lse;
+  const bool split = plan_splits(plan);
   const size_t rows = (size_t)batch * n_q_max * hq * plan.n_split;
-  prm.part_o = static_cast<float*>(ws);
-  prm.part_ml = plan.n_split > 1 ? reinterpret_cast<float2*>(
-                                       static_cast<char*>(ws) +
-                                       align256(rows * head_dim * sizeof(float)))
-                                 : nullptr;
+  prm.part_o = split ? static_cast<uint16_t*>(ws) : nullptr;
+  prm.part_ml = split ? reinterpret_cast<float2*>(static_cast<char*>(ws) +
+                                                  align256(rows * head_dim * sizeof(uint16_t)))
+                      : nullptr;
   prm.batch = batch;
   prm.hq = hq;
   prm.hkv = hkv;
   prm.n_q_max = n_q_max;
   prm.mask_words = mask_words;
-  prm.n_cg = plan.n_cg;
+  prm.n_cg_full = plan.n_cg_full;
   prm.n_split = plan.n_split;
-  prm.tps = plan.tiles_per_split;
+  prm.n_split_tail = plan.n_split_tail;
   prm.scale_log2 = scale * kLog2e;
   switch (head_dim) {
     case 32: return launch_d<32>(prm, plan, stream);

@@ -31,9 +31,9 @@ hipError_t launch_tree(const float* logp, const int32_t* ids, const int32_t* roo
 
 // ---- stage 3 --------------------------------------------------------------
 struct AttnPlan {
-  int n_cg;             // column groups per (request, kv head)
-  int n_split;          // key splits
-  int tiles_per_split;  // 32-key tiles per split
+  int n_cg_full;     // column groups of 256 columns per (request, kv head)
+  int n_split;       // key splits of each full group
+  int n_split_tail;  // key splits of the trailing partial group (0: none)
 };
 AttnPlan attn_plan(int batch, int hq, int hkv, int n_q_max, int max_kv_len);
 size_t attn_workspace_bytes(int batch, int hq, int hkv, int head_dim, int n_q_max,

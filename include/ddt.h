@@ -162,8 +162,9 @@ int ddt_build_tree(const float* topk_logp, const int32_t* topk_ids, const int32_
  * workspace: ddt_masked_attention_workspace_size(desc) bytes (split-KV
  *   partial results); contents on entry are ignored.
  * Errors: EINVAL if batch < 1, hq < 1, hkv < 1, hq % hkv != 0, n_q_max < 1,
- *         max_kv_len < 1, mask_words < ceil(n_q_max/64) with a mask, or a
- *         required pointer is NULL; EUNSUPPORTED if D is not 32, 64 or 128.
+ *         max_kv_len < 1 or > 2^22, mask_words < ceil(n_q_max/64) with a
+ *         mask, a required pointer is NULL, or q / k_cache / v_cache / out
+ *         is not 16-byte aligned; EUNSUPPORTED if D is not 32, 64 or 128.
  * Preconditions (device): prefix_len[r] + n_q[r] <= desc->max_kv_len and
  *   every referenced cache row exists.
  * ---------------------------------------------------------------------- */

@@ -103,6 +103,7 @@ def test_attention_validation(lib):
     assert _attn(lib, d(mask_words=4)) == E.DDT_EINVAL
     assert _attn(lib, d(batch=0)) == E.DDT_EINVAL
     assert _attn(lib, d(max_kv_len=0)) == E.DDT_EINVAL
+    assert _attn(lib, d(max_kv_len=(1 << 22) + 1)) == E.DDT_EINVAL
     assert _attn(lib, d(), q=None) == E.DDT_EINVAL
     assert _attn(lib, d(), q=ctypes.c_void_p(258)) == E.DDT_EINVAL     # misaligned
     assert _attn(lib, d(), ws=None) == E.DDT_EWORKSPACE
