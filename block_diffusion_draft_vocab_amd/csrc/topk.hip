@@ -4,18 +4,27 @@
 // over the vocabulary for every masked block position; the tree is built from
 // their log-probabilities.  This pass reads the logits once from HBM.
 //
-// Design (HBM-bound stream, two launches):
-//   topk_partial  grid (chunks, rows).  Each workgroup streams one chunk of a
-//                 row with 16-byte loads into registers, reduces (max, sum of
-//                 exp) and extracts the chunk's exact top-K (block_topk).
-//   topk_merge    one workgroup per row: log-sum-exp of the chunk partials and
-//                 the top-K of the chunk lists (block_topk again).
-// block_topk avoids sorting networks: a lower bound T on the K-th largest
-// key is the K-th largest of 64..256 group maxima; the few keys >= T are
-// gathered in LDS and ranked by counting.
+// Design (HBM-bound stream, two launches, every phase a few hundred cycles):
+//   topk_partial  grid (chunks, rows), 256 threads.  The chunk (<= 8192
+//                 floats) is streamed into registers with 16-byte loads;
+//                 block max, then the sum of exp(x - max); then the chunk's
+//                 exact top-K:
+//                   each wave takes T_w = the kw-th largest of its 64 lane
+//                   maxima (kw = ceil(K / busy waves)); T = min over the
+//                   waves, so at least K keys are >= T and every top-K key
+//                   is;
+//                   the few keys >= T are gathered in LDS (wave-aggregated
+//                   appends) and each finds its rank by counting greater
+//                   candidates (LDS broadcast reads).
+//   topk_merge    one workgroup per row: log-sum-exp of the chunk partials;
+//                 T = K-th largest of the first ceil(K/C) keys of the C
+//                 sorted chunk lists; a binary search per list counts its
+//                 keys >= T; those are compacted and ranked by counting.
 // Keys are 64-bit: order-preserving bits of x on top, ~id below, so a larger
 // key is a larger x and, among equal x, a smaller id.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -23,264 +32,350 @@
 namespace ddt {
 namespace {
 
-constexpr int kCandCap = 256;
-constexpr int kMergeMaxLists = 2 * kWave;  // lists the merge wave can own
-constexpr int kMergeMaxKeys = 8192;        // staged in LDS by the merge
+constexpr int kWaves = kTopkThreads / kWave;  // 4
+constexpr int kCandCap = 512;
+constexpr int kMergeMaxLists = 128;
+constexpr int kMergeMaxKeys = 8192;  // staged in LDS by the merge
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint64_t make_key(float x, int id) {
   return ((uint64_t)f32_order(x) << 32) | (uint64_t)(~(uint32_t)id);
 }
 
-__device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s2) {
-  const float M = fmaxf(m, m2);
-  if (M == -INFINITY) {
-    m = M;
-    s = 0.f;
-    return;
-  }
-  s = s * expf(m - M) + s2 * expf(m2 - M);
-  m = M;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-struct SelectSmem {
-  uint64_t tmax[kTopkThreads];
-  uint64_t gmax[kTopkThreads];
-  uint64_t cand[kCandCap];
-  uint64_t thr;
+// Wave-wide max / sum, result in every lane: DPP within rows of 16, then the
+// four row results.
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto dpp = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  v = max(v, dpp(v, std::integral_constant<int, 0xB1>{}));
+  v = max(v, dpp(v, std::integral_constant<int, 0x4E>{}));
+  v = max(v, dpp(v, std::integral_constant<int, 0x141>{}));
+  v = max(v, dpp(v, std::integral_constant<int, 0x140>{}));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Rank of key v among cand[0..n) (number of greater keys), reading the
+// candidates two at a time as 16-byte LDS broadcasts (cand 16-byte aligned).
+__device__ __forceinline__ int rank_among(const uint64_t* cand, int n, uint64_t v) {
+  const uint4* c2 = reinterpret_cast<const uint4*>(cand);
+  int rank = 0;
+#pragma unroll 4
+  for (int u = 0; u < n / 2; ++u) {
+    const uint4 q = c2[u];
+    const uint64_t a = ((uint64_t)q.y << 32) | q.x, b = ((uint64_t)q.w << 32) | q.z;
+    rank += (a > v) + (b > v);
+  }
+  if (n & 1) rank += cand[n - 1] > v;
+  return rank;
+}
+
+struct PartialSmem {
+  uint32_t lanemax[kTopkThreads];  // order-mapped thread maxima
+  float wmax[kWaves];
+  float wsum[kWaves];
+  uint32_t thr[kWaves];
   int cand_n;
+  alignas(16) uint64_t cand[kCandCap];
 };
-
-// Top-k (k <= 128) of the 64-bit keys spread over the block, E per thread
-// (0 = empty slot), written sorted descending to out[0..k).  Exact:
-//   T = k-th largest of G group maxima (G = 64, 128 or 256 groups of
-//       threads, the smallest with G >= 2k) -- at least k keys are >= T, so
-//       every top-k key is >= T;
-//   the keys >= T (about k of them) are gathered in LDS; each finds its
-//   rank by counting the greater candidates and lands at out[rank].
-// Keys are distinct (the low half is the token id), so ranks are too.
-// More than kCandCap candidates (massive ties) fall back to k rounds of a
-// block-wide arg-max.  Every thread must call it.
-template <int E>
-__device__ void block_topk(const uint64_t (&key)[E], int k, uint64_t* out, SelectSmem& sm) {
-  const int tid = threadIdx.x;
-  uint64_t tm = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) tm = key[e] > tm ? key[e] : tm;
-  sm.tmax[tid] = tm;
-  if (tid == 0) {
-    sm.cand_n = 0;
-    sm.thr = 1;
-  }
-  __syncthreads();
-  const int G = k <= 32 ? 64 : (k <= 64 ? 128 : 256);
-  uint64_t gm = 0;
-  if (tid < G) {
-    for (int t = tid; t < kTopkThreads; t += G) gm = sm.tmax[t] > gm ? sm.tmax[t] : gm;
-    sm.gmax[tid] = gm;
-  }
-  __syncthreads();
-  if (tid < G && gm != 0) {
-    int rank = 0;
-    for (int u = 0; u < G; ++u) rank += sm.gmax[u] > gm;
-    if (rank == k - 1) sm.thr = gm;
-  }
-  __syncthreads();
-  const uint64_t thr = sm.thr;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (key[e] >= thr) {
-      const int pos = atomicAdd(&sm.cand_n, 1);
-      if (pos < kCandCap) sm.cand[pos] = key[e];
-    }
-  }
-  __syncthreads();
-  const int n = sm.cand_n;
-  if (n <= kCandCap) {
-    if (tid < n) {
-      const uint64_t v = sm.cand[tid];
-      int rank = 0;
-      for (int u = 0; u < n; ++u) rank += sm.cand[u] > v;
-      if (rank < k) out[rank] = v;
-    }
-    for (int j = n + tid; j < k; j += kTopkThreads) out[j] = 0ull;
-    return;
-  }
-  // exact fallback: k rounds of block-wide max below the previous pick
-  uint64_t prev = ~0ull;
-  for (int j = 0; j < k; ++j) {
-    uint64_t b = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (key[e] < prev && key[e] > b) b = key[e];
-    __syncthreads();
-    sm.tmax[tid] = b;
-    __syncthreads();
-    for (int w = kTopkThreads / 2; w > 0; w >>= 1) {
-      if (tid < w && sm.tmax[tid + w] > sm.tmax[tid]) sm.tmax[tid] = sm.tmax[tid + w];
-      __syncthreads();
-    }
-    prev = sm.tmax[0];
-    if (tid == 0) out[j] = prev;
-  }
-}
 
 __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     const float* __restrict__ logits, int64_t ld, int vocab, int k, float inv_t, int chunk_len,
     int n_chunks, uint64_t* __restrict__ part_key, float2* __restrict__ part_ms) {
-  __shared__ SelectSmem sm;
-  __shared__ float red_m[kTopkThreads / kWave];
-  __shared__ float red_s[kTopkThreads / kWave];
-
+  __shared__ PartialSmem sm;
   const int chunk = blockIdx.x;
   const int row = blockIdx.y;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
   const float* rp = logits + (int64_t)row * ld;
   const int c0 = chunk * chunk_len;
   const int c1 = min(vocab, c0 + chunk_len);
   const bool vec = ((ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
 
+  // element i of this thread is index c0 + ((i/4) * 256 + tid) * 4 + i%4.
+  // Every load is issued unconditionally (out-of-range ones from c0), so
+  // all of them are in flight together; the values are masked afterwards.
   float x[kTopkPerThread];
+  if (vec) {
+    float4 v[kTopkPerThread / 4];
 #pragma unroll
-  for (int q = 0; q < kTopkPerThread / 4; ++q) {
-    const int base = c0 + (q * kTopkThreads + tid) * 4;
-    if (vec && base + 3 < c1) {
-      const float4 v = *reinterpret_cast<const float4*>(rp + base);
-      x[4 * q + 0] = v.x * inv_t;
-      x[4 * q + 1] = v.y * inv_t;
-      x[4 * q + 2] = v.z * inv_t;
-      x[4 * q + 3] = v.w * inv_t;
-    } else {
+    for (int q = 0; q < kTopkPerThread / 4; ++q) {
+      const int b = c0 + (q * kTopkThreads + tid) * 4;
+      v[q] = *reinterpret_cast<const float4*>(rp + (b + 3 < c1 ? b : c0 & ~3));
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = base + e;
-        x[4 * q + e] = idx < c1 ? rp[idx] * inv_t : -INFINITY;
+    for (int q = 0; q < kTopkPerThread / 4; ++q) {
+      const int b = c0 + (q * kTopkThreads + tid) * 4;
+      const bool full = b + 3 < c1;
+      x[4 * q + 0] = full ? v[q].x * inv_t : -INFINITY;
+      x[4 * q + 1] = full ? v[q].y * inv_t : -INFINITY;
+      x[4 * q + 2] = full ? v[q].z * inv_t : -INFINITY;
+      x[4 * q + 3] = full ? v[q].w * inv_t : -INFINITY;
+      if (!full && b < c1) {  // the one group that straddles the chunk end
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * q + e] = b + e < c1 ? rp[b + e] * inv_t : -INFINITY;
+      }
+    }
+  } else {
+    float y[kTopkPerThread];
+#pragma unroll
+    for (int i = 0; i < kTopkPerThread; ++i) {
+      const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
+      y[i] = rp[idx < c1 ? idx : c0];
+    }
+#pragma unroll
+    for (int i = 0; i < kTopkPerThread; ++i) {
+      const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
+      x[i] = idx < c1 ? y[i] * inv_t : -INFINITY;
+    }
+  }
+  float tm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kTopkPerThread; ++i) tm = fmaxf(tm, x[i]);
+  const float wm = wave_max_f(tm);
+  sm.lanemax[tid] = f32_order(tm);
+  if (lane == 0) sm.wmax[wid] = wm;
+  if (tid == 0) sm.cand_n = 0;
+  __syncthreads();
+
+  // block max, this thread's sum of exp(x - max)
+  const float M = fmaxf(fmaxf(sm.wmax[0], sm.wmax[1]), fmaxf(sm.wmax[2], sm.wmax[3]));
+  float s = 0.f;
+  if (M != -INFINITY) {
+    const float mb = M * kLog2e;
+#pragma unroll
+    for (int i = 0; i < kTopkPerThread; ++i) s += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mb));
+  }
+  const float ws = wave_sum_f(s);
+  if (lane == 0) sm.wsum[wid] = ws;
+  // Per-wave threshold.  With nw non-empty waves and kw = ceil(k / nw):
+  // a wave with >= kw valid lanes takes T_w = its kw-th largest lane
+  // maximum (>= kw of its keys are >= T_w); a wave with fewer valid lanes
+  // takes T_w = 0 (all its keys); an empty wave does not vote.  Then
+  // T = min T_w leaves at least k keys (or all of them) >= T.
+  {
+    const int len = c1 - c0;
+    const int lanes = min(kTopkThreads, (len + 3) / 4);
+    const int nw = (lanes + kWave - 1) / kWave;
+    const int kw = (k + nw - 1) / nw;
+    const bool me_valid = tm != -INFINITY;
+    const uint32_t me = me_valid ? sm.lanemax[tid] : 0u;
+    const uint4* lm4 = reinterpret_cast<const uint4*>(sm.lanemax + wid * kWave);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kWave / 4; ++j) {
+      const uint4 q = lm4[j];
+      cnt += (q.x >= me) + (q.y >= me) + (q.z >= me) + (q.w >= me);
+    }
+    // invalid lanes hold f32_order(-inf) > 0 in lanemax; they are never
+    // >= a valid lane's value, so cnt of a valid lane counts valid lanes only
+    const uint32_t t = wave_max_u32(me_valid && cnt >= kw ? me : 0u);
+    const uint64_t any_valid = __ballot(me_valid);
+    if (lane == 0) sm.thr[wid] = any_valid == 0 ? 0xFFFFFFFFu : t;
+  }
+  __syncthreads();
+
+  uint32_t T = sm.thr[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) T = sm.thr[w] < T ? sm.thr[w] : T;
+  if (tid == 0) {
+    const float S = (sm.wsum[0] + sm.wsum[1]) + (sm.wsum[2] + sm.wsum[3]);
+    part_ms[(int64_t)row * n_chunks + chunk] = make_float2(M, S);
+  }
+  // gather the keys >= T (T == 0 means every valid key, i.e. every finite
+  // x): the wave's count from per-slot ballots, one LDS atomic per wave,
+  // then one pass over the element slots that any lane of the wave selected
+  {
+    const float tf = T == 0u ? -3.402823466e38f : f32_unorder(T);
+    int total = 0;
+#pragma unroll
+    for (int i = 0; i < kTopkPerThread; ++i) total += __popcll(__ballot(x[i] >= tf));
+    int base = 0;
+    if (lane == 0 && total > 0) base = atomicAdd(&sm.cand_n, total);
+    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+    for (int i = 0; i < kTopkPerThread; ++i) {
+      const bool take = x[i] >= tf;
+      const uint64_t bal = __ballot(take);
+      if (bal != 0) {
+        if (take) {
+          const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+          const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
+          if (pos < kCandCap) sm.cand[pos] = make_key(x[i], idx);
+        }
+        base += __popcll(bal);
       }
     }
   }
+  __syncthreads();
 
-  // (max, sum exp) of this thread, then of the block
-  float m = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kTopkPerThread; ++i) m = fmaxf(m, x[i]);
-  float s = 0.f;
+  uint64_t* out = part_key + ((int64_t)row * n_chunks + chunk) * k;
+  const int n = sm.cand_n;
+  if (n <= kCandCap) {
+    for (int t = tid; t < n; t += kTopkThreads) {
+      const uint64_t v = sm.cand[t];
+      const int rank = rank_among(sm.cand, n, v);
+      if (rank < k) out[rank] = v;
+    }
+    for (int j = n + tid; j < k; j += kTopkThreads) out[j] = 0ull;
+    return;
+  }
+  // exact fallback for massive ties: k rounds of a block-wide arg-max
   uint64_t key[kTopkPerThread];
 #pragma unroll
   for (int i = 0; i < kTopkPerThread; ++i) {
     const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
-    const bool ok = idx < c1;
-    if (ok) s += __expf(x[i] - m);
-    key[i] = ok ? make_key(x[i], idx) : 0ull;
+    key[i] = idx < c1 ? make_key(x[i], idx) : 0ull;
   }
+  uint64_t* red = sm.cand;  // reused: kTopkThreads <= kCandCap
+  uint64_t prev = ~0ull;
+  for (int j = 0; j < k; ++j) {
+    uint64_t b = 0;
 #pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) {
-    const float m2 = __shfl_xor(m, d, kWave);
-    const float s2 = __shfl_xor(s, d, kWave);
-    ms_combine(m, s, m2, s2);
-  }
-  if ((tid & (kWave - 1)) == 0) {
-    red_m[tid / kWave] = m;
-    red_s[tid / kWave] = s;
-  }
-  block_topk<kTopkPerThread>(key, k, part_key + ((int64_t)row * n_chunks + chunk) * k, sm);
-  if (tid == 0) {
-    float M = red_m[0], S = red_s[0];
-    for (int w = 1; w < kTopkThreads / kWave; ++w) ms_combine(M, S, red_m[w], red_s[w]);
-    part_ms[(int64_t)row * n_chunks + chunk] = make_float2(M, S);
+    for (int i = 0; i < kTopkPerThread; ++i)
+      if (key[i] < prev && key[i] > b) b = key[i];
+    __syncthreads();
+    red[tid] = b;
+    __syncthreads();
+    for (int w = kTopkThreads / 2; w > 0; w >>= 1) {
+      if (tid < w && red[tid + w] > red[tid]) red[tid] = red[tid + w];
+      __syncthreads();
+    }
+    prev = red[0];
+    if (tid == 0) out[j] = prev;
   }
 }
 
-// One workgroup per row.  The chunk lists (each sorted descending) are
-// staged in LDS, then:
-//   S = the first m entries of every list (m = ceil(2k / n_chunks), |S| <=
-//       kCandCap), T = k-th largest of S -- k entries of S are >= T, so
-//       every top-k entry of the row is >= T;
-//   candidates = the prefix of every list that is >= T (about k entries);
-//   each candidate's rank = number of greater candidates -> out[rank].
-// Over kCandCap candidates (massive ties) falls back to a k-step merge of
-// the list heads.  Also combines the chunks' (max, sum of exp) into the
-// row's log-sum-exp.
+struct MergeSmem {
+  alignas(16) uint64_t cand[kCandCap];
+  int cnt[kMergeMaxLists + 1];
+  uint64_t thr;
+  float lse;
+};
+
+// One workgroup per row over the n_chunks sorted lists of k keys.
 __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
     const uint64_t* __restrict__ part_key, const float2* __restrict__ part_ms, int n_chunks,
     int k, int32_t* __restrict__ ids, float* __restrict__ logp, float* __restrict__ lse_out) {
-  extern __shared__ uint64_t lk[];  // [n_chunks * k]
-  __shared__ uint64_t cand[kCandCap];
-  __shared__ int cnt[kMergeMaxLists + 1];
-  __shared__ uint64_t thr_s;
-  __shared__ float lse_s;
+  extern __shared__ __attribute__((aligned(16))) uint64_t lk[];  // [n_chunks * k]
+  __shared__ MergeSmem sm;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
   const int n = n_chunks * k;
   const uint64_t* lists = part_key + (int64_t)row * n;
-  for (int i = tid; i < n; i += kTopkThreads) lk[i] = lists[i];
+  {
+    // 16-byte staging (k * 8 bytes per list; n even whenever k is)
+    const int n2 = n / 2;
+    const uint4* src = reinterpret_cast<const uint4*>(lists);
+    uint4* dst = reinterpret_cast<uint4*>(lk);
+    for (int i = tid; i < n2; i += kTopkThreads) dst[i] = src[i];
+    if ((n & 1) && tid == 0) lk[n - 1] = lists[n - 1];
+  }
   if (tid < kWave) {
-    float m = -INFINITY, sm = 0.f;
-    for (int c = tid; c < n_chunks; c += kWave) {
-      const float2 p = part_ms[(int64_t)row * n_chunks + c];
-      ms_combine(m, sm, p.x, p.y);
+    // log-sum-exp of the chunk partials (two passes over <= 128 pairs)
+    float2 p0 = tid < n_chunks ? part_ms[(int64_t)row * n_chunks + tid] : make_float2(-INFINITY, 0.f);
+    float2 p1 = tid + kWave < n_chunks ? part_ms[(int64_t)row * n_chunks + tid + kWave]
+                                       : make_float2(-INFINITY, 0.f);
+    const float M = wave_max_f(fmaxf(p0.x, p1.x));
+    float s = 0.f;
+    if (M != -INFINITY) {
+      if (p0.x != -INFINITY) s += p0.y * __builtin_amdgcn_exp2f((p0.x - M) * kLog2e);
+      if (p1.x != -INFINITY) s += p1.y * __builtin_amdgcn_exp2f((p1.x - M) * kLog2e);
     }
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) {
-      const float m2 = __shfl_xor(m, d, kWave);
-      const float s2 = __shfl_xor(sm, d, kWave);
-      ms_combine(m, sm, m2, s2);
-    }
-    if (tid == 0) {
-      lse_s = m + logf(sm);
-      thr_s = 1;
-    }
+    const float S = wave_sum_f(s);
+    if (lane == 0) sm.lse = M + logf(S);
   }
   __syncthreads();
-  int mm = (2 * k + n_chunks - 1) / n_chunks;
-  if (mm > k) mm = k;
-  while (n_chunks * mm > kCandCap) --mm;
-  const int ns = n_chunks * mm;
+
+  // T = k-th largest of the first mm keys of every list (n_chunks * mm >= k
+  // keys, all distinct), so at least k keys of the row are >= T.  Chunk
+  // lists shorter than k end in 0 keys, which are never >= T.
+  const int mm = (k + n_chunks - 1) / n_chunks;
+  const int ns = n_chunks * mm;  // <= k + n_chunks <= 256
+  if (tid < ns) sm.cand[tid] = lk[(tid / mm) * k + (tid % mm)];
+  __syncthreads();
   if (tid < ns) {
-    const uint64_t v = lk[(tid / mm) * k + (tid % mm)];
-    if (v != 0) {
-      int rank = 0;
-      for (int u = 0; u < ns; ++u) rank += lk[(u / mm) * k + (u % mm)] > v;
-      if (rank == k - 1) thr_s = v;
-    }
+    const uint64_t v = sm.cand[tid];
+    if (rank_among(sm.cand, ns, v) == k - 1) sm.thr = v;
   }
   __syncthreads();
-  const uint64_t T = thr_s;
+  const uint64_t T = sm.thr;
+  // keys >= T per list: the list is sorted descending, binary search
   if (tid < n_chunks) {
-    int j = 0;
-    while (j < k && lk[tid * k + j] >= T) ++j;
-    cnt[tid] = j;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      const int t = cnt[c];
-      cnt[c] = run;
-      run += t;
+    const uint64_t* L = lk + tid * k;
+    int lo = 0, hi = k;  // first index with L[i] < T
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (L[mid] >= T) lo = mid + 1;
+      else hi = mid;
     }
-    cnt[n_chunks] = run;
+    sm.cnt[tid] = lo;
   }
   __syncthreads();
-  const int nc = cnt[n_chunks];
-  const float lse = lse_s;
+  if (tid < kWave) {
+    // exclusive scan of the <= 128 counts, two per lane
+    const int a = 2 * tid < n_chunks ? sm.cnt[2 * tid] : 0;
+    const int b = 2 * tid + 1 < n_chunks ? sm.cnt[2 * tid + 1] : 0;
+    const int inc = wave_inclusive_scan(a + b);
+    const int ex = inc - (a + b);
+    if (2 * tid < n_chunks) sm.cnt[2 * tid] = ex;
+    if (2 * tid + 1 < n_chunks) sm.cnt[2 * tid + 1] = ex + a;
+    if (tid == kWave - 1) sm.cnt[n_chunks] = inc;
+  }
+  __syncthreads();
+  const int nc = sm.cnt[n_chunks];  // >= k, about k
+  const float lse = sm.lse;
   if (nc <= kCandCap) {
     if (tid < n_chunks) {
-      const int o = cnt[tid];
-      const int len = cnt[tid + 1] - o;
-      for (int j = 0; j < len; ++j) cand[o + j] = lk[tid * k + j];
+      const int o = sm.cnt[tid];
+      const int len = (tid + 1 < n_chunks ? sm.cnt[tid + 1] : nc) - o;
+      for (int j = 0; j < len; ++j) sm.cand[o + j] = lk[tid * k + j];
     }
     __syncthreads();
-    if (tid < nc) {
-      const uint64_t v = cand[tid];
-      int rank = 0;
-      for (int u = 0; u < nc; ++u) rank += cand[u] > v;
+    for (int t = tid; t < nc; t += kTopkThreads) {
+      const uint64_t v = sm.cand[t];
+      const int rank = rank_among(sm.cand, nc, v);
       if (rank < k) {
         ids[(int64_t)row * k + rank] = (int32_t)(~(uint32_t)v);
         logp[(int64_t)row * k + rank] = f32_unorder((uint32_t)(v >> 32)) - lse;
       }
     }
   } else if (tid < kWave) {
-    // k-step merge of the list heads (lane owns lists lane and lane + 64)
-    const int lane = tid;
+    // massive ties: k-step merge of the list heads (lane owns lists lane
+    // and lane + 64)
     int pos[2] = {0, 0};
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
@@ -355,7 +450,7 @@ hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, i
                      stream, logits, ld, vocab, k, inv_t, p.chunk_len, p.n_chunks, part_key,
                      part_ms);
   const size_t smem = (size_t)p.n_chunks * k * sizeof(uint64_t);
-  if (smem > 64 * 1024)
+  if (smem > 32 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   hipLaunchKernelGGL(topk_merge_kernel, dim3(n_rows), dim3(kTopkThreads), smem, stream, part_key,
