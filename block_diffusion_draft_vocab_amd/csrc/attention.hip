@@ -689,7 +689,10 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int n_q_max, int max_kv_len) {
     plan.n_split = clamp_split(s);
     plan.n_split_tail = tail_split(plan.n_split);
   } else {
-    plan.n_split = clamp_split(kCUs / (tail > 0 ? tail : 1));
+    // only a partial group per head (drafter-sized queries): half a
+    // workgroup per CU, so every workgroup gets two or more tiles and the
+    // split merge has half as many partials to read (measured fastest)
+    plan.n_split = clamp_split(kCUs / 2 / (tail > 0 ? tail : 1));
     plan.n_split_tail = tail_waves > 0 ? plan.n_split : 0;
   }
   return plan;

@@ -40,14 +40,15 @@ __device__ inline void bitonic_sort_desc(uint64_t* a, int n) {
   }
 }
 
-// Inclusive prefix sum across one wavefront.
+// Inclusive prefix sum across one wavefront (DPP: shifts of 1, 2, 4, 8
+// inside each row of 16 lanes, then the row totals broadcast forward).
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int t = __shfl_up(v, d, kWave);
-    if (lane >= d) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 

@@ -13,10 +13,9 @@
 //   for depth d = 2..L:
 //     parents := depth-(d-1) members of G, in G order (index j)
 //     children (j, rank) with key > theta and (j+1)(rank+1) <= B; the
-//       children of one parent form a descending run
-//     G := top B of (G u runs): each key's rank is found by counting the
-//       greater keys of every run (binary search where a run straddles it),
-//       and the keys ranked below B are scattered to their rank
+//       children of one parent form a descending run, whose length a binary
+//       search over the ranks finds
+//     G := top B of (G u runs), merged by pairwise merge-path rounds
 //     theta := G[B-1]
 //
 // Why it is exact: a node's key is below its parent's and its elder
@@ -127,80 +126,103 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     y[i] = logp[((int64_t)r * L + d) * K + rk];
   }
   __syncthreads();
+  // gb: G (sorted, g keys) with the level's children appended after it;
+  // obuf: the other buffer of the merge ping-pong
+  uint64_t* gb = keys;
+  uint64_t* obuf = kbuf;
   int g = min(k_tree, B);
-  for (int i = tid; i < g; i += nt) keys[i] = tkey(y[i], 1, 0, i);
+  for (int i = tid; i < g; i += nt) gb[i] = tkey(y[i], 1, 0, i);
   __syncthreads();
-  uint64_t theta = (g == B && B > 0) ? keys[B - 1] : 0ull;
-
-  // Level-local index of the depth-dd members among G positions [0, g):
-  // one ballot per wave chunk of 64 positions, a prefix over the chunks.
-  // Returns the count; idx_out[q] gets the index of position q (members).
-  auto index_depth = [&](int dd, int* idx_out) -> int {
-    const int nchunk = (g + kWave - 1) / kWave;
-    for (int c = wid; c < nchunk; c += nt / kWave) {
-      const int q = c * kWave + lane;
-      const bool is = q < g && key_depth(keys[q]) == dd;
-      const uint64_t bal = __ballot(is);
-      if (lane == 0) wcnt[c] = __popcll(bal);
-      if (is) idx_out[q] = __popcll(bal & lanemask_lt());
-    }
-    __syncthreads();
-    if (tid < kWave) {  // nchunk <= 32: one wave scans the chunk counts
-      const int t = tid < nchunk ? wcnt[tid] : 0;
-      const int inc = wave_inclusive_scan(t);
-      if (tid < nchunk) wcnt[tid] = inc - t;
-      if (tid == kWave - 1) misc[0] = inc;
-    }
-    __syncthreads();
-    for (int q = tid; q < g; q += nt)
-      if (key_depth(keys[q]) == dd) idx_out[q] += wcnt[q / kWave];
-    const int total = misc[0];
-    __syncthreads();
-    return total;
-  };
+  uint64_t theta = (g == B && B > 0) ? gb[B - 1] : 0ull;
+  const int nwaves = nt / kWave;
 
   for (int d = 2; d <= L && g > 0; ++d) {
-    // parents: the depth d-1 members of G, numbered in G order
-    const int n = index_depth(d - 1, slot_tab);
+    // parents: the depth d-1 members of G, numbered in G order (a ballot
+    // per 64-position chunk, then the chunk counts summed directly)
+    const int nchunk = (g + kWave - 1) / kWave;
+    for (int c = wid; c < nchunk; c += nwaves) {
+      const int q = c * kWave + lane;
+      const bool is = q < g && key_depth(gb[q]) == d - 1;
+      const uint64_t bal = __ballot(is);
+      if (lane == 0) wcnt[c] = __popcll(bal);
+      if (is) slot_tab[q] = __popcll(bal & lanemask_lt());
+    }
+    __syncthreads();
+    int n = 0;
+    for (int c = 0; c < nchunk; ++c) n += wcnt[c];
     if (n == 0) break;
     for (int q = tid; q < g; q += nt) {
-      const uint64_t kq = keys[q];
-      if (key_depth(kq) == d - 1) pscore[slot_tab[q]] = key_score(kq);
+      const uint64_t kq = gb[q];
+      if (key_depth(kq) != d - 1) continue;
+      int pre = 0;
+      for (int c = 0; c < q / kWave; ++c) pre += wcnt[c];
+      pscore[pre + slot_tab[q]] = key_score(kq);
     }
-    for (int j = tid; j < n; j += nt) rcnt[j] = 0;
     __syncthreads();
-    // candidates (j, c): key above theta and (j+1)(c+1) <= B; for one
-    // parent they form a prefix of ranks, so counting them gives the run
+    // run length of parent j: children (j, c) with key above theta and
+    // (j+1)(c+1) <= B; keys fall with c, so a binary search finds it.
+    // Thread t owns parents [t*per, t*per + per).
+    // (n <= B < 2 * nt: the launch gives max(cand_cap, 1024) threads or more)
     const float* yd = y + (d - 1) * k_tree;
-    const int items = n * k_tree;
-    for (int it = tid; it < items; it += nt) {
-      const int j = it / k_tree;
-      const int c = it - j * k_tree;
-      if ((j + 1) * (c + 1) <= B && tkey(pscore[j] + yd[c], d, j, c) > theta)
-        atomicAdd(&rcnt[j], 1);
+    const int per = (n + nt - 1) / nt;
+    int lens[2] = {0, 0};
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = tid * per + u;
+      int len = 0;
+      if (u < per && j < n) {
+        int lo = 0, hi = min(k_tree, B / (j + 1));
+        const float ps = pscore[j];
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (tkey(ps + yd[mid], d, j, mid) > theta) lo = mid + 1;
+          else hi = mid;
+        }
+        len = lo;
+      }
+      lens[u] = len;
+      mine += len;
     }
+    // block exclusive scan of the per-thread totals
+    const int inc = wave_inclusive_scan(mine);
+    if (lane == kWave - 1) misc[8 + wid] = inc;
     __syncthreads();
-    // run layout: run 0 = G at [0, g), run j+1 = children of parent j
-    const int nc = block_scan_array(rcnt, n, misc + 8);   // rcnt -> offsets
+    int wpre = 0, nc = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      const int t = misc[8 + w];
+      wpre += w < wid ? t : 0;
+      nc += t;
+    }
+    {
+      int o = wpre + inc - mine;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = tid * per + u;
+        if (u < per && j < n) rcnt[j] = o;
+        o += lens[u];
+      }
+    }
     if (nc == 0) break;
+    __syncthreads();
+    // children keys after G: run 0 = G at [0, g), run j+1 = parent j's
+    const int items = n * k_tree;
     for (int it = tid; it < items; it += nt) {
       const int j = it / k_tree;
       const int c = it - j * k_tree;
       const int o = rcnt[j];
       const int len = (j + 1 < n ? rcnt[j + 1] : nc) - o;
-      if (c < len) keys[g + o + c] = tkey(pscore[j] + yd[c], d, j, c);
+      if (c < len) gb[g + o + c] = tkey(pscore[j] + yd[c], d, j, c);
     }
-    for (int j = tid; j <= n + 1; j += nt) {
-      // offsets of runs 0..n, and the end
+    for (int j = tid; j <= n + 1; j += nt)  // offsets of runs 0..n, and the end
       roff[j] = j == 0 ? 0 : (j <= n ? g + rcnt[j - 1] : g + nc);
-    }
     __syncthreads();
     // pairwise merge-path rounds: runs (2i, 2i+1) -> run i, every output
     // element placed independently by a binary search on its diagonal
     const int total = g + nc;
     int R = n + 1;
-    uint64_t* src = keys;
-    uint64_t* dst = kbuf;
+    uint64_t* src = gb;
+    uint64_t* dst = obuf;
     int* ro = roff;
     int* ro_next = roff2;
     while (R > 1) {
@@ -233,12 +255,13 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       int* u = ro; ro = ro_next; ro_next = u;
       R = Rn;
     }
+    gb = src;
+    obuf = dst;
     g = min(B, total);
-    if (src != keys)
-      for (int i = tid; i < g; i += nt) keys[i] = src[i];
-    __syncthreads();
-    theta = (g == B) ? keys[B - 1] : 0ull;
+    theta = (g == B) ? gb[B - 1] : 0ull;
   }
+  __syncthreads();
+  keys = gb;
 
   // ---- flatten: slot of every node, parent slots, outputs, ancestor mask
   // level-local index of every node within its depth, all depths at once:
