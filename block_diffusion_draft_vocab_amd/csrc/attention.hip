@@ -21,8 +21,9 @@
 // Per 64-key tile
 //   staging: K and V rows are copied global -> LDS by the load unit itself
 //     (global_load_lds_dwordx4, no registers involved), the 16-byte chunks
-//     of each row XOR-swizzled by (row & 7) against bank conflicts; a ring
-//     of three tiles keeps the copies two tiles ahead, one barrier per tile.
+//     of each row XOR-swizzled against bank conflicts (one swizzle for the
+//     K reads, another for the transposing V reads); a ring of three tiles
+//     keeps the copies two tiles ahead, one barrier per tile.
 //   S^T (keys x cols) = K . Q^T     v_mfma_f32_32x32x16_bf16, two 32-key
 //     halves = two independent accumulation chains.  Each lane then holds 16
 //     keys of ONE column per half, so a row reduction needs one exchange
@@ -64,8 +65,20 @@ constexpr int kCUs = 256;
 template <int D>
 struct Geo {
   static constexpr int kCh = D / 8;                        // 16-byte chunks per key row
-  static constexpr int kSwz = kCh < 8 ? kCh - 1 : 7;       // chunk XOR mask
   static constexpr int kRowBytes = D * 2;
+  // Physical 16-byte chunk of logical chunk c in tile row r is c ^ swz(r).
+  // K: the sixteen lanes a ds_read_b128 serves together read one logical
+  // chunk of sixteen consecutive rows, which must land in sixteen different
+  // bank groups.  V: a ds_read_b64_tr_b16 lane group reads two adjacent
+  // chunks of four consecutive rows, which must land in eight different
+  // bank groups.  (Measured: 284 and 129 B/clk per CU, the instructions'
+  // full rates, against 164 and 84 with a plain row & 7 swizzle.)
+  static __device__ __forceinline__ int swz_k(int r) {
+    return D == 128 ? (r & 15) : (D == 64 ? ((r >> 1) & 7) : (r & 3));
+  }
+  static __device__ __forceinline__ int swz_v(int r) {
+    return D == 128 ? 2 * (r & 3) : (D == 64 ? (r & 2) : (r & 3));
+  }
   static constexpr int kTileBytes = kKT * kRowBytes;       // one K or V tile
   static constexpr int kLoads = 2 * kKT * kCh / kThreads;  // 16-byte copies per thread per tile
   static constexpr int kSmem = 2 * kRing * kTileBytes;     // K ring, then V ring
@@ -301,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     const bool isv = G::kLoads == 1 ? wid >= 4 : j >= G::kLoads / 2;
     const int Lt = isv ? L - kPer : L;
     ld_row[j] = Lt / G::kCh;
-    ld_col[j] = ((Lt % G::kCh) ^ (ld_row[j] & G::kSwz)) * 8;
+    ld_col[j] = ((Lt % G::kCh) ^ (isv ? G::swz_v(ld_row[j]) : G::swz_k(ld_row[j]))) * 8;
     ld_lds[j] = (uint32_t)((Lt - lane) * 16) + (isv ? kRing * G::kTileBytes : 0);
   }
   auto issue_tile = [&](int t, int slot) {
@@ -318,20 +331,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     }
   };
 
-  // Q and, when the split starts inside the prefix, its first two tiles
-  // (always processed) are put in flight before the tile list is built
+  // Q, then the split's first two tiles, are put in flight before the tile
+  // list is built.  Prefix tiles are always processed; a range that starts
+  // in the own rows is copied speculatively and re-copied below in the rare
+  // case that the list skips one of those tiles.
+  // (the Q loads are inline asm: the compiler cannot tell them apart from
+  // the tile copies issued after them and would wait for all of them)
   bf16x8 qf[D / 16];
   {
-    const uint16_t* qp = p.q + (((int64_t)r * p.n_q_max + qi) * p.hq + head) * D;
+    const uint16_t* qp = p.q + (((int64_t)r * p.n_q_max + qi) * p.hq + head) * D + 8 * h2;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t)
-      qf[t] = valid ? *reinterpret_cast<const bf16x8*>(qp + 16 * t + 8 * h2) : bf16x8{};
+      asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[t]) : "v"(qp + 16 * t));
   }
-  const bool early = t_end - t_begin >= 2 && (t_begin + 2) * kKT <= P;
-  if (early) {
-    issue_tile(t_begin, 0);
-    issue_tile(t_begin + 1, 1);
-  }
+  const int n_spec = min(2, t_end - t_begin);
+  issue_tile(t_begin, 0);
+  if (n_spec > 1) issue_tile(t_begin + 1, 1);
 
   // ---- tiles to process: every tile holding prefix keys, and the own-row
   // tiles in which some column of the workgroup sees a key.  The visibility
@@ -376,10 +391,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 
   // ---- per-lane LDS read offsets inside one slot.
   // K as the A operand of S^T: row n (+32 for the second half), logical
-  // chunk 2tt + h2, physical chunk (2tt) ^ (h2 ^ (n & swz)).
+  // chunk 2tt + h2, physical chunk (2tt) ^ (h2 ^ swz_k(n)).
   uint32_t koff[D / 16];
   {
-    const int w = h2 ^ (n & G::kSwz);
+    const int w = h2 ^ G::swz_k(n);  // rows n and n + 32 share the swizzle
 #pragma unroll
     for (int tt = 0; tt < D / 16; ++tt)
       koff[tt] = (uint32_t)(n * G::kRowBytes + (((2 * tt) ^ w) * 16));
@@ -394,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     const int q4 = lane >> 4, e = (lane >> 2) & 3, rr = lane & 3;
     const int row = (q4 >> 1) * 4 + e;
     const int y = (q4 & 1) * 2 + (rr >> 1);
-    const int z = y ^ (row & G::kSwz);
+    const int z = y ^ G::swz_v(row);  // unchanged by the +8 / +16 row offsets
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       voff[u] = (uint32_t)(row * G::kRowBytes + (((4 * u) ^ z) * 16) + (rr & 1) * 8);
@@ -406,14 +421,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
 
-  // prologue: everything is waited for before the loop, so inside it the
-  // only memory operations in flight are tile copies and "all but the
-  // newest tile" is a plain vmcnt
-  if (!early) {
+  // prologue: if the list does not start with the speculated tiles, let
+  // those copies land and copy the right ones.  Then Q and tile 0 are
+  // waited for (tile 1 may stay in flight: inside the loop the only memory
+  // operations in flight are tile copies, so "all but the newest tile" is a
+  // plain vmcnt).
+  if ((ntl > 0 && tile_at(0) != t_begin) || (ntl > 1 && n_spec > 1 && tile_at(1) != t_begin + 1) ||
+      (ntl > 1 && n_spec < 2)) {
+    wait_vm<0>();
+    __builtin_amdgcn_s_barrier();  // every wave's speculative copies have landed
+    __asm__ volatile("" ::: "memory");
     if (ntl > 0) issue_tile(tile_at(0), 0);
     if (ntl > 1) issue_tile(tile_at(1), 1);
   }
-  wait_vm<0>();
+  if (ntl > 1) wait_vm<G::kLoads>();
+  else wait_vm<0>();
+  // Q was issued before every tile copy, so it has landed; columns past the
+  // end (loaded from row 0 of the request) are zeroed
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    asm volatile("" : "+v"(qf[t]));
+    if (!valid) qf[t] = bf16x8{};
+  }
 
   for (int i = 0; i < ntl; ++i) {
     // this tile's copies done (the next tile's may stay in flight), then
@@ -529,13 +558,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
                                                         pf[c], o[dt], 0, 0, 0);
     });
   }
+  // ---- result rows (bf16): the output itself without splits, else this
+  // split's partial, normalised by its own sum.  The O^T fragments scatter
+  // 8-byte pieces over 32 rows, so each wave first transposes its 32 rows
+  // through LDS (the tile ring is free once every wave is past the loop)
+  // and then writes whole rows with 16-byte stores.
+  constexpr int kRowPad = D * 2 + 16;  // bytes per staged row (pad: bank spread)
+  __syncthreads();
   if (!wave_active) return;
-
   const float l_tot = xor32_sum(l_run);
-  if (!valid) return;
-  const int64_t rowid = ((int64_t)r * p.n_q_max + qi) * p.hq + head;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  uint16_t* op = SPLIT ? p.part_o + (rowid * p.n_split + s) * D : p.out + rowid * D;
+  const uint32_t stage = lds0 + wid * (kColsPerWave * kRowPad);
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -545,13 +578,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         h[e] = __builtin_bit_cast(uint16_t, (__bf16)(o[dt][a * 4 + e] * inv));
-      uint2 w;
-      w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-      w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-      *reinterpret_cast<uint2*>(op + d0) = w;
+      typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+      const u32x2 w = {(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                       (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+      *(LDS_AS u32x2*)(uintptr_t)(stage + n * kRowPad + d0 * 2) = w;
     }
   }
-  if (h2 == 0) {
+  if (valid && h2 == 0) {
+    const int64_t rowid = ((int64_t)r * p.n_q_max + qi) * p.hq + head;
     if constexpr (SPLIT) {
       p.part_ml[rowid * p.n_split + s] = make_float2(m_run, l_tot);
     } else {
@@ -559,17 +593,35 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
         p.lse[rowid] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     }
   }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // D/8 lanes per row, 64 / (D/8) rows per instruction
+  constexpr int kLpr = D / 8;
+  constexpr int kRpi = 64 / kLpr;
+#pragma unroll
+  for (int rr = 0; rr < kColsPerWave; rr += kRpi) {
+    const int row = rr + lane / kLpr;
+    const int chunk = lane % kLpr;
+    const int c = col0 + wid * kColsPerWave + row;
+    const u32x4 v = *(const LDS_AS u32x4*)(uintptr_t)(stage + row * kRowPad + chunk * 16);
+    if (c < ncols) {
+      const int64_t rowid = ((int64_t)r * p.n_q_max + c / g) * p.hq + hk * g + c % g;
+      uint16_t* op = SPLIT ? p.part_o + (rowid * p.n_split + s) * D : p.out + rowid * D;
+      *reinterpret_cast<u32x4*>(op + chunk * 8) = v;
+    }
+  }
 }
 
 // Merge of the key splits: one group of D/8 threads per (request, query
 // row, q-head), each thread owning 8 consecutive output elements (16-byte
-// partial loads and stores).  Splits are read 8 at a time with all 16 loads
+// partial loads and stores).  Splits are read 16 at a time with all 32 loads
 // in flight, merged into a running (max, weighted sum) like the tile loop.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
   constexpr int kTPR = D / 8;
   constexpr int kRPB = 256 / kTPR;
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   const int gid = blockIdx.x * kRPB + threadIdx.x / kTPR;
   const int lane = threadIdx.x % kTPR;
   if (gid >= p.batch * p.n_q_max * p.hq) return;
