@@ -50,6 +50,9 @@ def parse():
                     help="launch every stage from Python instead of replaying one HIP graph "
                          "per input set")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--no-streams", action="store_true",
+                    help="skip the extra logit-stream measurements (target argmax over the "
+                         "verify logits, the 512-row top-K pass)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (a plain copy kernel of "
                          "known size, to scale HBM byte counters) and exit")
@@ -66,6 +69,83 @@ def calibrate_copy(mib: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_mib": mib, "launches": 5, "bytes_read_per_launch": n * 4,
                       "bytes_written_per_launch": n * 4}))
+
+
+def time_graph(torch, fns, reps):
+    """Average device time of one call: a HIP graph holds every call of fns
+    back to back and is replayed reps times between HIP events recorded on
+    the launch stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e-3 / (reps * len(fns))
+
+
+def stream_passes(args, torch, ddt, synth, dev):
+    """HBM-bound logit passes beside the step: the target's greedy tokens over
+    the verify logits (257 tree slots x 151936, ddt_argmax) and the 512-row
+    top-16 pass of the serving batch.  Cold: the calls rotate over input sets
+    larger together than the 256 MB last-level cache; warm: one set again."""
+    out = {}
+    V = synth.QWEN3_VOCAB
+    n_slots = synth.CONFIGS[3].B + 1
+    log(args, "target argmax: generating 4 x 257-row verify logit sets")
+    sets = [torch.from_numpy(synth.make_verify_logits(args.seed + 77 + i, n_slots)[0]).to(dev)
+            for i in range(4)]
+    ids = torch.empty(n_slots, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(1, ddt.argmax_workspace_size(n_slots, V)), dtype=torch.uint8,
+                     device=dev)
+    nbytes = n_slots * V * 4 + n_slots * 4
+    for mode, bufs in (("cold", sets), ("warm", [sets[0]] * 4)):
+        t = time_graph(torch, [lambda b=b: ddt.argmax(b, ids=ids, workspace=ws) for b in bufs],
+                       50)
+        out[mode] = t
+    out = {
+        "rows": n_slots, "vocab": V, "algorithmic_bytes": nbytes,
+        "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "achieved": round(nbytes / out["cold"] / 1e9, 1),
+        "frac": round(nbytes / out["cold"] / 1e9 / HBM_PEAK_GBS, 4),
+        "us_cold": round(out["cold"] * 1e6, 3), "us_warm": round(out["warm"] * 1e6, 3),
+        "achieved_warm": round(nbytes / out["warm"] / 1e9, 1),
+    }
+    del sets
+    c5 = synth.CONFIGS[5]
+    rows, K = c5.batch * c5.L, c5.K
+    log(args, f"top-{K} pass: generating 2 x {rows}-row logit sets")
+    big = []
+    for i in range(2):
+        z, _ = synth.make_logits(np.random.Generator(np.random.PCG64(args.seed + 99 + i)), c5)
+        big.append(torch.from_numpy(z).to(dev))
+    tids = torch.empty(rows, K, dtype=torch.int32, device=dev)
+    tlogp = torch.empty(rows, K, dtype=torch.float32, device=dev)
+    tws = torch.empty(ddt.topk_workspace_size(rows, V, K), dtype=torch.uint8, device=dev)
+    tb = rows * V * 4 + rows * K * 8
+    t = time_graph(torch, [lambda b=b: ddt.topk_logprobs(b, K, 1.0, ids=tids, logp=tlogp,
+                                                        want_lse=False, workspace=tws)
+                           for b in big * 2], 25)
+    del big
+    c5out = {"rows": rows, "vocab": V, "K": K, "algorithmic_bytes": tb, "bound": "hbm",
+             "peak": HBM_PEAK_GBS, "unit": "GB/s", "us_cold": round(t * 1e6, 3),
+             "achieved": round(tb / t / 1e9, 1), "frac": round(tb / t / 1e9 / HBM_PEAK_GBS, 4)}
+    return out, c5out
 
 
 def log(args, msg):
@@ -333,6 +413,9 @@ def main():
         },
     }
 
+    if not args.no_streams:
+        result["target_argmax"], result["logit_pass_512rows"] = stream_passes(
+            args, torch, ddt, synth, dev)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cases[0], args.cpu_seconds, args)
     print(json.dumps(result), flush=True)

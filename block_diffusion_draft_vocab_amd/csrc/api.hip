@@ -55,6 +55,24 @@ DDT_EXPORT int ddt_topk_logprobs(const float* logits, int64_t ld_logits, int n_r
                                         static_cast<hipStream_t>(stream)));
 }
 
+// ---- target argmax --------------------------------------------------------
+DDT_EXPORT size_t ddt_argmax_workspace_size(int n_rows, int vocab) {
+  if (n_rows < 1 || vocab < 1) return 0;
+  return ddt::argmax_workspace_bytes(n_rows, vocab);
+}
+
+DDT_EXPORT int ddt_argmax(const float* logits, int64_t ld_logits, int n_rows, int vocab,
+                          int32_t* out_ids, float* out_max, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (n_rows < 1 || vocab < 1 || ld_logits < vocab) return DDT_EINVAL;
+  if (logits == nullptr || out_ids == nullptr) return DDT_EINVAL;
+  if (n_rows > ddt::kArgmaxMaxRows) return DDT_EUNSUPPORTED;
+  const size_t need = ddt::argmax_workspace_bytes(n_rows, vocab);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return DDT_EWORKSPACE;
+  return launch_status(ddt::launch_argmax(logits, ld_logits, n_rows, vocab, out_ids, out_max,
+                                          workspace, static_cast<hipStream_t>(stream)));
+}
+
 // ---- stage 2 ---------------------------------------------------------------
 static bool tree_args_ok(int batch, int L, int k, int k_tree, int budget) {
   return batch >= 1 && L >= 1 && L <= 32 && k >= 1 && k_tree >= 1 && k_tree <= k &&

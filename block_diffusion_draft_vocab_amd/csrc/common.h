@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ddt {
 
 constexpr int kWave = 64;  // CDNA wavefront width
@@ -17,6 +19,14 @@ __device__ __forceinline__ uint32_t f32_order(float x) {
 __device__ __forceinline__ float f32_unorder(uint32_t o) {
   uint32_t b = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
   return __uint_as_float(b);
+}
+
+// 16-byte streaming load (non-temporal hint: the line is not kept for
+// reuse), for data read exactly once such as a pass over the logits.
+__device__ __forceinline__ float4 load_f4_stream(const float* p) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 t = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+  return make_float4(t.x, t.y, t.z, t.w);
 }
 
 // Descending bitonic sort of n (a power of two) 64-bit keys held in LDS.
@@ -95,6 +105,62 @@ __device__ inline int block_scan_array(int* arr, int n, int* scratch) {
   }
   __syncthreads();
   return total;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Wave-wide max / sum, result in every lane: DPP within rows of 16, then the
+// four row results.
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto dpp = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  v = max(v, dpp(v, std::integral_constant<int, 0xB1>{}));
+  v = max(v, dpp(v, std::integral_constant<int, 0x4E>{}));
+  v = max(v, dpp(v, std::integral_constant<int, 0x141>{}));
+  v = max(v, dpp(v, std::integral_constant<int, 0x140>{}));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  auto dpp = [](uint32_t x, auto ctrl) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xF, 0xF, false);
+  };
+  v = min(v, dpp(v, std::integral_constant<int, 0xB1>{}));
+  v = min(v, dpp(v, std::integral_constant<int, 0x4E>{}));
+  v = min(v, dpp(v, std::integral_constant<int, 0x141>{}));
+  v = min(v, dpp(v, std::integral_constant<int, 0x140>{}));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return min(min(r0, r1), min(r2, r3));
 }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {

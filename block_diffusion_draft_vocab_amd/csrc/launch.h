@@ -22,6 +22,20 @@ hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, i
                        float inv_t, int32_t* ids, float* logp, float* lse, void* ws,
                        hipStream_t stream);
 
+// ---- target argmax (the verifier's greedy tokens) ------------------------
+struct ArgmaxPlan {
+  int n_chunks;
+  int chunk_len;  // multiple of 4, <= kArgmaxMaxChunk
+};
+constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxPerThread = 32;
+constexpr int kArgmaxMaxChunk = kArgmaxThreads * kArgmaxPerThread;  // 8192
+constexpr int kArgmaxMaxRows = 65535;  // rows are grid.y
+ArgmaxPlan argmax_plan(int n_rows, int vocab);
+size_t argmax_workspace_bytes(int n_rows, int vocab);
+hipError_t launch_argmax(const float* logits, int64_t ld, int n_rows, int vocab, int32_t* ids,
+                         float* maxv, void* ws, hipStream_t stream);
+
 // ---- stage 2 --------------------------------------------------------------
 size_t tree_smem_bytes(int L, int k_tree, int budget);
 hipError_t launch_tree(const float* logp, const int32_t* ids, const int32_t* root, int batch,

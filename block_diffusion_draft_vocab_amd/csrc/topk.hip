@@ -42,49 +42,6 @@ __device__ __forceinline__ uint64_t make_key(float x, int id) {
   return ((uint64_t)f32_order(x) << 32) | (uint64_t)(~(uint32_t)id);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Wave-wide max / sum, result in every lane: DPP within rows of 16, then the
-// four row results.
-__device__ __forceinline__ float wave_max_f(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
-  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-__device__ __forceinline__ float wave_sum_f(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  v += dpp_f<0x140>(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  auto dpp = [](uint32_t x, auto ctrl) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, decltype(ctrl)::value, 0xF, 0xF, false);
-  };
-  v = max(v, dpp(v, std::integral_constant<int, 0xB1>{}));
-  v = max(v, dpp(v, std::integral_constant<int, 0x4E>{}));
-  v = max(v, dpp(v, std::integral_constant<int, 0x141>{}));
-  v = max(v, dpp(v, std::integral_constant<int, 0x140>{}));
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
-  return max(max(r0, r1), max(r2, r3));
-}
-
 // Rank of key v among cand[0..n) (number of greater keys), reading the
 // candidates two at a time as 16-byte LDS broadcasts (cand 16-byte aligned).
 __device__ __forceinline__ int rank_among(const uint64_t* cand, int n, uint64_t v) {
@@ -121,7 +78,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
   const float* rp = logits + (int64_t)row * ld;
   const int c0 = chunk * chunk_len;
   const int c1 = min(vocab, c0 + chunk_len);
-  const bool vec = ((ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0);
+  // 16-byte loads need aligned rows and at least one whole 4-float group
+  // (c0 is a multiple of 4, so the group at c0 is then in bounds)
+  const bool vec = ((ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15) == 0) &&
+                   c1 - c0 >= 4;
 
   // element i of this thread is index c0 + ((i/4) * 256 + tid) * 4 + i%4.
   // Every load is issued unconditionally (out-of-range ones from c0), so
@@ -132,7 +92,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
 #pragma unroll
     for (int q = 0; q < kTopkPerThread / 4; ++q) {
       const int b = c0 + (q * kTopkThreads + tid) * 4;
-      v[q] = *reinterpret_cast<const float4*>(rp + (b + 3 < c1 ? b : c0 & ~3));
+      v[q] = load_f4_stream(rp + (b + 3 < c1 ? b : c0));
     }
 #pragma unroll
     for (int q = 0; q < kTopkPerThread / 4; ++q) {
@@ -435,7 +395,7 @@ size_t topk_workspace_bytes(int n_rows, int vocab, int k) {
 
 bool topk_supported(int n_rows, int vocab, int k) {
   const TopkPlan p = topk_plan(n_rows, vocab, k);
-  return p.chunk_len <= kTopkMaxChunk && p.n_chunks <= kMergeMaxLists &&
+  return n_rows <= 65535 && p.chunk_len <= kTopkMaxChunk && p.n_chunks <= kMergeMaxLists &&
          p.n_chunks * k <= kMergeMaxKeys;
 }
 

@@ -31,6 +31,8 @@ SIGNATURES = {
     "ddt_status_string": (_c.c_char_p, [_I]),
     "ddt_topk_logprobs_workspace_size": (_SZ, [_I, _I, _I]),
     "ddt_topk_logprobs": (_I, [_P, _I64, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
+    "ddt_argmax_workspace_size": (_SZ, [_I, _I]),
+    "ddt_argmax": (_I, [_P, _I64, _I, _I, _P, _P, _P, _SZ, _P]),
     "ddt_build_tree_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "ddt_build_tree": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "ddt_masked_attention_workspace_size": (_SZ, [_P]),
@@ -131,6 +133,33 @@ def topk_logprobs(logits: torch.Tensor, k: int, inv_temperature: float = 1.0, *,
                                _ptr(ids), _ptr(logp), _ptr(lse), _ptr(ws), wsb, _stream(stream))
     _check("ddt_topk_logprobs", st)
     return ids, logp, lse
+
+
+# ---------------------------------------------------------------- target argmax
+def argmax_workspace_size(n_rows: int, vocab: int) -> int:
+    return int(load().ddt_argmax_workspace_size(n_rows, vocab))
+
+
+def argmax(logits: torch.Tensor, *, vocab: Optional[int] = None, ids=None, maxv=None,
+           want_max: bool = False, workspace=None, stream=None):
+    """Per-row arg-max (smallest id among the maxima) of device float32 logits.
+    Returns (ids i32 [rows], max f32 [rows] or None)."""
+    lib = load()
+    if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_cuda:
+        raise ValueError("logits must be a device float32 [rows, ld] tensor")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    rows, ld = logits.shape[0], logits.stride(0)
+    vocab = logits.shape[1] if vocab is None else vocab
+    dev = logits.device
+    ids = torch.empty(rows, dtype=torch.int32, device=dev) if ids is None else ids
+    if want_max and maxv is None:
+        maxv = torch.empty(rows, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(argmax_workspace_size(rows, vocab), dev, workspace)
+    st = lib.ddt_argmax(_ptr(logits), ld, rows, vocab, _ptr(ids), _ptr(maxv), _ptr(ws), wsb,
+                        _stream(stream))
+    _check("ddt_argmax", st)
+    return ids, maxv
 
 
 # ---------------------------------------------------------------- stage 2

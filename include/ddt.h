@@ -12,6 +12,8 @@
  *                            block (drafter pass over injected context KV)
  *   4. ddt_accept_compact    greedy acceptance walk against the target's
  *                            argmax tokens + compaction of the accepted KV rows
+ * and, between 3 and 4, ddt_argmax: the target's greedy token per tree slot
+ * (a vocab-wide arg-max over the verify logits).
  *
  * Pages the operations come from (cited by title and section):
  *   [DDTree]  "Accelerating Speculative Decoding with Block Diffusion Draft
@@ -78,13 +80,46 @@ const char* ddt_status_string(int status);
  *            contents on entry are ignored.
  * Errors: EINVAL if n_rows < 1, vocab < 1, k < 1, k > vocab, k > 128,
  *         ld_logits < vocab, a required pointer is NULL, or
- *         inv_temperature is not a positive finite number.
+ *         inv_temperature is not a positive finite number; EUNSUPPORTED if
+ *         n_rows > 65535.
  * Preconditions (device): logits finite.
  * ---------------------------------------------------------------------- */
 size_t ddt_topk_logprobs_workspace_size(int n_rows, int vocab, int k);
 int ddt_topk_logprobs(const float* logits, int64_t ld_logits, int n_rows, int vocab,
                       int k, float inv_temperature, int32_t* topk_ids, float* topk_logp,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Target argmax: the verifier's greedy token for every tree slot.
+ *
+ * [DDTree] "방법론 자세히 보기" (method in detail): the target model runs once
+ * over the flattened tree and the verifier compares its outputs with the
+ * tree; with greedy decoding the output at a slot is the target's most
+ * probable token there.  These ids are the target_argmax input of
+ * ddt_accept_compact.
+ *
+ * For each row r (0 <= r < n_rows):
+ *   out_ids[r] = the smallest v in [0, vocab) with
+ *                logits[r*ld_logits + v] = max_u logits[r*ld_logits + u]
+ *   out_max[r] = that maximum (a maximum of -0 is reported as +0; -0 and +0
+ *                tie, and the smaller index wins)
+ * No temperature: the arg-max of z/T equals that of z for T > 0 up to ties
+ * created by rounding, and greedy verification uses the raw logits.
+ *
+ * logits    f32 [n_rows, ld_logits] (only the first vocab columns are read)
+ * out_ids   i32 [n_rows]  (output)
+ * out_max   f32 [n_rows]  (output, may be NULL)
+ * workspace ddt_argmax_workspace_size() bytes of device scratch (chunk
+ *           partials; 0 -- workspace may be NULL -- when a row fits one
+ *           chunk); contents on entry are ignored.
+ * Errors: EINVAL if n_rows < 1, vocab < 1, ld_logits < vocab, or logits /
+ *         out_ids is NULL; EUNSUPPORTED if n_rows > 65535; EWORKSPACE if
+ *         the workspace is needed and missing or too small.
+ * Preconditions (device): no NaN among the logits (+-inf is allowed).
+ * ---------------------------------------------------------------------- */
+size_t ddt_argmax_workspace_size(int n_rows, int vocab);
+int ddt_argmax(const float* logits, int64_t ld_logits, int n_rows, int vocab, int32_t* out_ids,
+               float* out_max, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Stage 2: DDTree best-first tree build, flattened.

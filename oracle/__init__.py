@@ -10,6 +10,7 @@ Each function is the plain definition of one step of the chain, written for a
 reader to check against the pages by eye:
 
 * ``logits.topk_logprobs``     per-position log-softmax + top-K
+* ``logits.argmax_rows``       the target's greedy token per tree slot
 * ``tree.build_tree``          DDTree best-first top-B prefix tree, flattened,
                                with parent/depth arrays and the ancestor mask
 * ``attention.masked_attention``  GQA attention over prefix KV + own KV with

@@ -6,7 +6,12 @@ position after the bonus token.  The tree builder consumes those per-position
 distributions as log-probabilities.  The pages fix no top-K; the candidate
 count K per position comes from the workload configuration.
 
-Definition computed here, per row:
+``argmax_rows`` is the verifier's greedy token ([DDTree] "방법론 자세히 보기",
+method in detail: the target's outputs at the tree slots are compared with the
+tree; at temperature 0 the output is the most probable token):
+  id = the smallest v with z_v = max_u z_u            (raw logits, no scaling)
+
+Definition computed by ``topk_logprobs``, per row:
   1. x_v = fl32(z_v * fl32(1/T))          (T = 1 leaves z unchanged)
   2. lse = m + log(sum_v exp(x_v - m))      in float64, m = max_v x_v
   3. the K ids with largest x, ties broken by smaller id first
@@ -42,3 +47,15 @@ def topk_logprobs(logits: np.ndarray, k: int, inv_temperature: float = 1.0):
         ids[r] = top
         logp[r] = (xr[top] - lse[r]).astype(np.float32)
     return ids, logp, lse
+
+
+def argmax_rows(logits: np.ndarray):
+    """Return (ids i32 [rows], max f32 [rows]): per row the smallest index
+    holding the row maximum (numpy's argmax returns the first occurrence)."""
+    z = np.asarray(logits, dtype=np.float32)
+    if z.ndim != 2 or z.shape[1] < 1:
+        raise ValueError("logits must be [rows, vocab] with vocab >= 1")
+    if np.isnan(z).any():
+        raise ValueError("NaN logits have no arg-max")
+    ids = np.argmax(z, axis=1).astype(np.int32)
+    return ids, z[np.arange(z.shape[0]), ids]

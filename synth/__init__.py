@@ -233,3 +233,16 @@ def force_path_target(node_token, node_parent, node_depth, n_nodes, stop_slot,
         tok = (tok + 1) % vocab
     t[stop_slot] = tok
     return t
+
+
+def make_verify_logits(seed: int, rows: int, vocab: int = QWEN3_VOCAB,
+                       peak: float = 12.0) -> tuple[np.ndarray, np.ndarray]:
+    """Target logits at the tree slots (one row per flattened slot):
+    float32 2*N(0,1) with +peak added at one seeded token per row, the shape
+    of a confident target distribution.  Returns (logits [rows, vocab],
+    planted ids [rows])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    z = (2.0 * rng.standard_normal((rows, vocab), dtype=np.float32)).astype(np.float32)
+    planted = rng.integers(0, vocab, size=rows, dtype=np.int64)
+    z[np.arange(rows), planted] += np.float32(peak)
+    return z, planted

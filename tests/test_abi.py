@@ -29,7 +29,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 11
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(ddt.SIGNATURES)
@@ -58,6 +58,32 @@ def test_topk_validation(lib):
     assert need > 0
     assert _topk(lib, wsb=need - 1) == E.DDT_EWORKSPACE
     assert lib.ddt_topk_logprobs_workspace_size(4, 1000, 2000) == 0
+
+
+def test_topk_rows_beyond_grid_limit(lib):
+    assert _topk(lib, rows=65536) == ddt.DDT_EUNSUPPORTED
+
+
+def _argmax(lib, logits=FAKE, ld=151936, rows=257, V=151936, ids=FAKE, maxv=None, ws=FAKE,
+            wsb=1 << 30):
+    return lib.ddt_argmax(logits, ld, rows, V, ids, maxv, ws, wsb, None)
+
+
+def test_argmax_validation(lib):
+    E = ddt
+    assert _argmax(lib, logits=None) == E.DDT_EINVAL
+    assert _argmax(lib, ids=None) == E.DDT_EINVAL
+    assert _argmax(lib, rows=0) == E.DDT_EINVAL
+    assert _argmax(lib, V=0, ld=0) == E.DDT_EINVAL
+    assert _argmax(lib, ld=151935) == E.DDT_EINVAL
+    assert _argmax(lib, rows=65536) == E.DDT_EUNSUPPORTED
+    need = lib.ddt_argmax_workspace_size(257, 151936)
+    assert need == 257 * 19 * 8                       # 19 chunk partials per row
+    assert _argmax(lib, ws=None) == E.DDT_EWORKSPACE
+    assert _argmax(lib, wsb=need - 1) == E.DDT_EWORKSPACE
+    # a row of at most one chunk needs no workspace
+    assert lib.ddt_argmax_workspace_size(4, 8192) == 0
+    assert lib.ddt_argmax_workspace_size(0, 8192) == 0
 
 
 def _tree(lib, batch=1, L=16, k=32, k_tree=32, B=256, logp=FAKE, mask=FAKE):

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle.logits import topk_logprobs
+from oracle.logits import argmax_rows, topk_logprobs
 
 
 def _rows(seed, rows, V):
@@ -111,3 +111,73 @@ def test_planted_token_is_rank0_in_tiny_config():
 def test_rejects_bad_k():
     with pytest.raises(ValueError):
         topk_logprobs(np.zeros((1, 4), np.float32), 5)
+
+
+# ---- argmax_rows: the target's greedy token -------------------------------
+def test_argmax_planted_positions():
+    """A value planted above every other entry is found wherever it sits,
+    including the first and last columns."""
+    rng = np.random.default_rng(11)
+    V = 151936
+    z = rng.uniform(-5, 5, size=(6, V)).astype(np.float32)
+    where = [0, V - 1, 8191, 8192, 77777, 4]
+    for r, j in enumerate(where):
+        z[r, j] = 6.0
+    ids, mx = argmax_rows(z)
+    assert ids.tolist() == where
+    assert np.all(mx == np.float32(6.0))
+
+
+def test_argmax_ties_go_to_smaller_id():
+    """Equal maxima: the smaller index wins, whatever their order of
+    planting and distance apart."""
+    z = np.zeros((4, 5000), dtype=np.float32)
+    z[0, [4999, 17]] = 2.0
+    z[1, [3, 4]] = 2.0
+    z[2, :] = -1.5                      # constant row: index 0
+    z[3, [4096, 4095, 9 * 4 + 1]] = 1e30
+    ids, mx = argmax_rows(z)
+    assert ids.tolist() == [17, 3, 0, 37]
+    assert mx.tolist() == [2.0, 2.0, -1.5, np.float32(1e30)]
+
+
+def test_argmax_infinities_and_signed_zero():
+    """-inf rows still have an arg-max (index 0); +inf dominates; -0 == +0
+    counts as a tie, so the earlier index wins."""
+    z = np.full((3, 10), -np.inf, dtype=np.float32)
+    z[1, 6] = np.inf
+    z[2, :] = -1.0
+    z[2, 5] = -0.0
+    z[2, 2] = 0.0
+    ids, _ = argmax_rows(z)
+    assert ids.tolist() == [0, 6, 2]
+
+
+def test_argmax_brute_force_tiny():
+    """Exhaustive over small integer-valued rows (many ties): the index that
+    maximises (value, -index), found by scanning every pair."""
+    rng = np.random.default_rng(5)
+    z = rng.integers(-3, 4, size=(300, 9)).astype(np.float32)
+    ids, _ = argmax_rows(z)
+    for r in range(z.shape[0]):
+        best = 0
+        for j in range(1, z.shape[1]):
+            if z[r, j] > z[r, best]:
+                best = j
+        assert ids[r] == best
+
+
+def test_argmax_is_rank0_of_topk():
+    """Cross-check against the top-K ranking (lexsort path) at T = 1."""
+    z = _rows(12, 16, 20000)
+    z[3, 100] = z[3, 99] = z[3].max() + 1.0          # a tie at the top
+    ids, _ = argmax_rows(z)
+    tk, _, _ = topk_logprobs(z, 1)
+    assert np.array_equal(ids, tk[:, 0])
+
+
+def test_argmax_rejects_nan():
+    z = np.zeros((1, 4), dtype=np.float32)
+    z[0, 2] = np.nan
+    with pytest.raises(ValueError):
+        argmax_rows(z)
