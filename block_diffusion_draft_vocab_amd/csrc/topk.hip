@@ -281,10 +281,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   __syncthreads();
 
   // T = k-th largest of the first mm keys of every list (n_chunks * mm >= k
-  // keys, all distinct), so at least k keys of the row are >= T.  Chunk
+  // keys, all distinct; mm is raised while the candidates fit 64, which
+  // tightens T), so at least k keys of the row are >= T.  Chunk
   // lists shorter than k end in 0 keys, which are never >= T.
-  const int mm = (k + n_chunks - 1) / n_chunks;
-  const int ns = n_chunks * mm;  // <= k + n_chunks <= 256
+  const int mm = max((k + n_chunks - 1) / n_chunks, min(k, kWave / n_chunks));
+  const int ns = n_chunks * mm;  // <= max(k + n_chunks, 64) <= 256
   if (tid < ns) sm.cand[tid] = lk[(tid / mm) * k + (tid % mm)];
   __syncthreads();
   if (tid < ns) {
@@ -367,6 +368,155 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   if (lse_out != nullptr && tid == 0) lse_out[row] = lse;
 }
 
+// Wave-level LDS hand-off: the wave's LDS writes are visible to all of its
+// lanes afterwards (no block barrier; other waves are not involved).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kWaveCandCap = 512;  // keys >= T a wave ranks in LDS
+
+// The same merge with one wave per row and no block barrier, for rows whose
+// n = n_chunks * k keys fit R per lane (n <= 64 R) and whose threshold
+// candidates fit one per lane (n_chunks * ceil(k / n_chunks) <= 64).  Each
+// lane holds R keys of the row in registers; the threshold T is
+// ranked among the candidates through a small LDS area of the wave; a wave
+// scan of the per-lane counts of keys >= T places those keys in LDS, and
+// each is ranked by counting the greater ones.
+template <int R>
+__global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
+    const uint64_t* __restrict__ part_key, const float2* __restrict__ part_ms, int n_rows,
+    int n_chunks, int k, int32_t* __restrict__ ids, float* __restrict__ logp,
+    float* __restrict__ lse_out) {
+  __shared__ alignas(16) uint64_t cand_all[kWaves][kWave];
+  __shared__ alignas(16) uint64_t take_all[kWaves][kWaveCandCap];
+  const int wid = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * kWaves + wid;
+  if (row >= n_rows) return;
+  const int n = n_chunks * k;
+  const uint64_t* lists = part_key + (int64_t)row * n;
+  // candidates: the first mm keys of every list, as many as fit one per
+  // lane (a larger set gives a tighter T and fewer keys to rank), at least
+  // ceil(k / n_chunks) so that at least k candidates exist
+  const int mm = max((k + n_chunks - 1) / n_chunks, min(k, kWave / n_chunks));
+  const int ns = n_chunks * mm;  // <= 64 (host check)
+
+  // all global loads first: keys, threshold candidates, chunk (max, sum)
+  // key r of this lane is key kidx(r) of the row: pairs of keys at 16-byte
+  // steps across the wave, so each load instruction reads 1 KB contiguous
+  // (the order of the keys inside the wave does not matter below: ranks
+  // come from comparisons only).  An odd n (16-byte alignment not
+  // guaranteed) takes 8-byte loads in the same order.
+  auto kidx = [&](int r) { return 2 * (lane + kWave * (r >> 1)) + (r & 1); };
+  uint64_t key[R];
+  if ((n & 1) == 0) {
+    const uint4* l4 = reinterpret_cast<const uint4*>(lists);
+#pragma unroll
+    for (int r = 0; r < R; r += 2) {
+      const int i = lane + kWave * (r >> 1);
+      const uint4 q = l4[2 * i < n ? i : 0];
+      key[r] = ((uint64_t)q.y << 32) | q.x;
+      key[r + 1] = ((uint64_t)q.w << 32) | q.z;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) key[r] = lists[kidx(r) < n ? kidx(r) : 0];
+  }
+  const uint64_t c = lists[lane < ns ? (lane / mm) * k + lane % mm : 0];
+  const float2* ms = part_ms + (int64_t)row * n_chunks;
+  const float2 p0 = ms[lane < n_chunks ? lane : 0];
+  const float2 p1 = ms[lane + kWave < n_chunks ? lane + kWave : 0];
+
+  // log-sum-exp of the chunk partials
+  float lse;
+  {
+    const float a = lane < n_chunks ? p0.x : -INFINITY;
+    const float b = lane + kWave < n_chunks ? p1.x : -INFINITY;
+    const float M = wave_max_f(fmaxf(a, b));
+    float s = 0.f;
+    if (M != -INFINITY) {
+      if (a != -INFINITY) s += p0.y * __builtin_amdgcn_exp2f((a - M) * kLog2e);
+      if (b != -INFINITY) s += p1.y * __builtin_amdgcn_exp2f((b - M) * kLog2e);
+    }
+    lse = M + logf(wave_sum_f(s));
+  }
+
+  // T = k-th largest candidate (0 -- take every key -- when that rank is
+  // only held by tied zero padding keys)
+  uint64_t* cw = cand_all[wid];
+  const uint64_t cv = lane < ns ? c : 0ull;
+  cw[lane] = cv;
+  wave_lds_sync();
+  const int crank = rank_among(cw, ns, cv);
+  const uint64_t hit = __ballot(lane < ns && crank == k - 1);
+  uint64_t T = 0;
+  if (hit != 0) {
+    const int src = __builtin_ctzll(hit);
+    T = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cv >> 32), src) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cv, src);
+  }
+
+  // this lane's keys >= T
+  int cnt = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) cnt += (kidx(r) < n) && key[r] >= T;
+  const int inc = wave_inclusive_scan(cnt);
+  const int nc = __builtin_amdgcn_readlane(inc, kWave - 1);
+  int32_t* oid = ids + (int64_t)row * k;
+  float* olp = logp + (int64_t)row * k;
+  if (nc <= kWaveCandCap) {
+    uint64_t* tw = take_all[wid];
+    int o = inc - cnt;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if ((kidx(r) < n) && key[r] >= T) tw[o++] = key[r];
+    }
+    wave_lds_sync();
+    for (int t = lane; t < nc; t += kWave) {
+      const uint64_t v = tw[t];
+      const int rank = rank_among(tw, nc, v);
+      if (rank < k) {
+        oid[rank] = (int32_t)(~(uint32_t)v);
+        olp[rank] = f32_unorder((uint32_t)(v >> 32)) - lse;
+      }
+    }
+  } else {
+    // massive ties: k-step merge of the list heads (lane owns lists lane
+    // and lane + 64), reading the lists from global memory
+    int pos[2] = {0, 0};
+    for (int j = 0; j < k; ++j) {
+      uint64_t best = 0;
+      int who = -1;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int cc = lane + h * kWave;
+        if (cc < n_chunks && pos[h] < k) {
+          const uint64_t hv = lists[cc * k + pos[h]];
+          if (hv > best) {
+            best = hv;
+            who = h;
+          }
+        }
+      }
+      uint64_t wb = best;
+#pragma unroll
+      for (int d = kWave / 2; d > 0; d >>= 1) {
+        const uint64_t o2 = shfl_xor_u64(wb, d);
+        wb = o2 > wb ? o2 : wb;
+      }
+      if (best == wb && wb != 0 && who >= 0) ++pos[who];
+      if (lane == 0) {
+        oid[j] = (int32_t)(~(uint32_t)wb);
+        olp[j] = f32_unorder((uint32_t)(wb >> 32)) - lse;
+      }
+    }
+  }
+  if (lse_out != nullptr && lane == 0) lse_out[row] = lse;
+}
+
 }  // namespace
 
 TopkPlan topk_plan(int n_rows, int vocab, int k) {
@@ -409,7 +559,21 @@ hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, i
   hipLaunchKernelGGL(topk_partial_kernel, dim3(p.n_chunks, n_rows), dim3(kTopkThreads), 0,
                      stream, logits, ld, vocab, k, inv_t, p.chunk_len, p.n_chunks, part_key,
                      part_ms);
-  const size_t smem = (size_t)p.n_chunks * k * sizeof(uint64_t);
+  const int n = p.n_chunks * k;
+  const int ns = p.n_chunks * ((k + p.n_chunks - 1) / p.n_chunks);
+  if (n <= 64 * 32 && ns <= kWave) {
+    const dim3 grid((n_rows + kWaves - 1) / kWaves);
+#define DDT_MERGE_WAVE(RR)                                                                    \
+  hipLaunchKernelGGL(topk_merge_wave_kernel<RR>, grid, dim3(kTopkThreads), 0, stream, part_key, \
+                     part_ms, n_rows, p.n_chunks, k, ids, logp, lse)
+    if (n <= 64 * 4) DDT_MERGE_WAVE(4);
+    else if (n <= 64 * 8) DDT_MERGE_WAVE(8);
+    else if (n <= 64 * 16) DDT_MERGE_WAVE(16);
+    else DDT_MERGE_WAVE(32);
+#undef DDT_MERGE_WAVE
+    return hipGetLastError();
+  }
+  const size_t smem = (size_t)n * sizeof(uint64_t);
   if (smem > 32 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);

@@ -80,6 +80,21 @@ def test_topk_ties(gpu):
     _compare(gpu, logits, 64)
 
 
+@pytest.mark.parametrize("k", [32, 64])
+def test_topk_ties_one_wave_merge(gpu, k):
+    """16 x 151936 with K = 32 / 64: the merge runs one wave per row.  A
+    constant row leaves about K lists' worth of keys at or above the
+    threshold (the exact head-merge fallback), a row of many equal maxima and
+    rows of coarse ties exercise the ranked path."""
+    rng = np.random.default_rng(8)
+    logits = np.round(rng.standard_normal((16, synth.QWEN3_VOCAB)), 1).astype(np.float32)
+    logits[1] = -0.25
+    logits[2, ::7] = logits[2].max()
+    logits[3, ::8192] = 9.0                           # one equal max per chunk start
+    logits[4, 8191::8192] = 9.0                       # ... and per chunk end
+    _compare(gpu, logits, k)
+
+
 def test_topk_temperature(gpu):
     rng = np.random.default_rng(6)
     logits = (3 * rng.standard_normal((8, 20000))).astype(np.float32)
