@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--no-streams", action="store_true",
                     help="skip the extra logit-stream measurements (target argmax over the "
-                         "verify logits, the 512-row top-K pass)")
+                         "verify logits, the 512-row top-K pass, the fused LM head)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run device-to-device copies of MIB MiB (a plain copy kernel of "
                          "known size, to scale HBM byte counters) and exit")
@@ -101,8 +101,9 @@ def time_graph(torch, fns, reps):
 
 def stream_passes(args, torch, ddt, synth, dev):
     """HBM-bound logit passes beside the step: the target's greedy tokens over
-    the verify logits (257 tree slots x 151936, ddt_argmax) and the 512-row
-    top-16 pass of the serving batch.  Cold: the calls rotate over input sets
+    the verify logits (257 tree slots x 151936, ddt_argmax), the 512-row
+    top-16 pass of the serving batch, and the fused LM head -> top-32 of the
+    16 drafter rows (ddt_lmhead_topk, a 151936 x 4096 bf16 head).  Cold: the calls rotate over input sets
     larger together than the 256 MB last-level cache; warm: one set again."""
     out = {}
     V = synth.QWEN3_VOCAB
@@ -145,7 +146,29 @@ def stream_passes(args, torch, ddt, synth, dev):
     c5out = {"rows": rows, "vocab": V, "K": K, "algorithmic_bytes": tb, "bound": "hbm",
              "peak": HBM_PEAK_GBS, "unit": "GB/s", "us_cold": round(t * 1e6, 3),
              "achieved": round(tb / t / 1e9, 1), "frac": round(tb / t / 1e9 / HBM_PEAK_GBS, 4)}
-    return out, c5out
+    # fused shared LM head -> top-32 for the 16 drafter rows (hidden 4096):
+    # the bf16 head is streamed once per call; two heads rotate (2.5 GB)
+    c3 = synth.CONFIGS[3]
+    L, hidden, K3 = c3.L, 4096, c3.K
+    log(args, "LM head: generating 2 x 151936 x 4096 bf16 heads on the device")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 123)
+    hs = torch.randn(L, hidden, device=dev, generator=gen).to(torch.bfloat16)
+    heads = [(torch.randn(V, hidden, device=dev, generator=gen) * (2.0 / 64.0)).to(torch.bfloat16)
+             for _ in range(2)]
+    lids = torch.empty(L, K3, dtype=torch.int32, device=dev)
+    llogp = torch.empty(L, K3, dtype=torch.float32, device=dev)
+    lws = torch.empty(ddt.lmhead_topk_workspace_size(L, hidden, V, K3), dtype=torch.uint8,
+                      device=dev)
+    t = time_graph(torch, [lambda w=w: ddt.lmhead_topk(hs, w, K3, ids=lids, logp=llogp,
+                                                       want_lse=False, workspace=lws)
+                           for w in heads * 2], 10)
+    del heads
+    lb = V * hidden * 2 + L * hidden * 2 + L * K3 * 8
+    lmout = {"rows": L, "hidden": hidden, "vocab": V, "K": K3, "algorithmic_bytes": lb,
+             "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", "us_cold": round(t * 1e6, 3),
+             "achieved": round(lb / t / 1e9, 1), "frac": round(lb / t / 1e9 / HBM_PEAK_GBS, 4)}
+    return out, c5out, lmout
 
 
 def log(args, msg):
@@ -414,8 +437,8 @@ def main():
     }
 
     if not args.no_streams:
-        result["target_argmax"], result["logit_pass_512rows"] = stream_passes(
-            args, torch, ddt, synth, dev)
+        (result["target_argmax"], result["logit_pass_512rows"],
+         result["lmhead_topk"]) = stream_passes(args, torch, ddt, synth, dev)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(cases[0], args.cpu_seconds, args)
     print(json.dumps(result), flush=True)

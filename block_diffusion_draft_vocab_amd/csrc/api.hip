@@ -55,6 +55,41 @@ DDT_EXPORT int ddt_topk_logprobs(const float* logits, int64_t ld_logits, int n_r
                                         static_cast<hipStream_t>(stream)));
 }
 
+// ---- fused LM head + log-softmax / top-K ------------------------------------
+static bool lmhead_args_ok(int n_rows, int hidden, int vocab, int k) {
+  return n_rows >= 1 && hidden >= 1 && vocab >= 1 && k >= 1 && k <= vocab;
+}
+static bool lmhead_supported(int n_rows, int hidden, int vocab, int k) {
+  const long nc = ddt::lmhead_chunks(vocab);
+  return hidden % 256 == 0 && hidden <= 4096 && k <= ddt::kLmMaxK &&
+         nc <= ddt::kTopkMergeMaxLists && nc * k <= ddt::kTopkMergeMaxKeys &&
+         (n_rows + 15) / 16 <= 65535;
+}
+
+DDT_EXPORT size_t ddt_lmhead_topk_workspace_size(int n_rows, int hidden, int vocab, int k) {
+  if (!lmhead_args_ok(n_rows, hidden, vocab, k) || !lmhead_supported(n_rows, hidden, vocab, k))
+    return 0;
+  return ddt::lmhead_workspace_bytes(n_rows, vocab, k);
+}
+
+DDT_EXPORT int ddt_lmhead_topk(const void* hidden_states, const void* weight, int n_rows,
+                               int hidden, int vocab, int k, float inv_temperature,
+                               int32_t* topk_ids, float* topk_logp, float* lse, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!lmhead_args_ok(n_rows, hidden, vocab, k)) return DDT_EINVAL;
+  if (hidden_states == nullptr || weight == nullptr || topk_ids == nullptr ||
+      topk_logp == nullptr)
+    return DDT_EINVAL;
+  if (!(inv_temperature > 0.f) || !isfinite(inv_temperature)) return DDT_EINVAL;
+  if (!aligned16(hidden_states) || !aligned16(weight)) return DDT_EINVAL;
+  if (!lmhead_supported(n_rows, hidden, vocab, k)) return DDT_EUNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < ddt::lmhead_workspace_bytes(n_rows, vocab, k))
+    return DDT_EWORKSPACE;
+  return launch_status(ddt::launch_lmhead_topk(hidden_states, weight, n_rows, hidden, vocab, k,
+                                               inv_temperature, topk_ids, topk_logp, lse,
+                                               workspace, static_cast<hipStream_t>(stream)));
+}
+
 // ---- target argmax --------------------------------------------------------
 DDT_EXPORT size_t ddt_argmax_workspace_size(int n_rows, int vocab) {
   if (n_rows < 1 || vocab < 1) return 0;

@@ -15,12 +15,34 @@ struct TopkPlan {
 constexpr int kTopkThreads = 256;
 constexpr int kTopkPerThread = 32;
 constexpr int kTopkMaxChunk = kTopkThreads * kTopkPerThread;  // 8192
+constexpr int kTopkMergeMaxLists = 256;   // chunk lists one merge handles per row
+constexpr int kTopkMergeMaxKeys = 16384;  // chunk lists x k
 TopkPlan topk_plan(int n_rows, int vocab, int k);
 bool topk_supported(int n_rows, int vocab, int k);
 size_t topk_workspace_bytes(int n_rows, int vocab, int k);
 hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, int k,
                        float inv_t, int32_t* ids, float* logp, float* lse, void* ws,
                        hipStream_t stream);
+
+// Merge of per-chunk partials (sorted key lists + (max, sum of exp)) into
+// the rows' top-k ids / log-probs / lse; shared by the logit pass and the
+// fused LM head.  n_chunks <= kTopkMergeMaxLists, n_chunks * k <=
+// kTopkMergeMaxKeys.
+hipError_t launch_topk_merge(const uint64_t* part_key, const float2* part_ms, int n_rows,
+                             int n_chunks, int k, int32_t* ids, float* logp, float* lse,
+                             hipStream_t stream);
+
+// ---- fused LM head + log-softmax / top-K --------------------------------
+constexpr int kLmThreads = 512;
+constexpr int kLmTilesPerWave = 5;                            // 16-column vocab tiles
+constexpr int kLmChunk = (kLmThreads / 64) * 16 * kLmTilesPerWave;  // 640 columns
+constexpr int kLmMaxK = 64;
+int lmhead_chunks(int vocab);
+size_t lmhead_smem_bytes(int hidden);
+size_t lmhead_workspace_bytes(int n_rows, int vocab, int k);
+hipError_t launch_lmhead_topk(const void* hs, const void* w, int n_rows, int hidden, int vocab,
+                              int k, float inv_t, int32_t* ids, float* logp, float* lse,
+                              void* ws, hipStream_t stream);
 
 // ---- target argmax (the verifier's greedy tokens) ------------------------
 struct ArgmaxPlan {

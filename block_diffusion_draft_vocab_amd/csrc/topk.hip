@@ -34,8 +34,9 @@ namespace {
 
 constexpr int kWaves = kTopkThreads / kWave;  // 4
 constexpr int kCandCap = 512;
-constexpr int kMergeMaxLists = 128;
-constexpr int kMergeMaxKeys = 8192;  // staged in LDS by the merge
+constexpr int kMergeMaxLists = kTopkMergeMaxLists;  // 256: one thread per list
+constexpr int kMergeMaxKeys = kTopkMergeMaxKeys;    // 16384: staged in LDS by the merge
+constexpr int kTopkPlanMaxLists = 128;  // chunk lists the logit pass itself plans
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ uint64_t make_key(float x, int id) {
@@ -265,15 +266,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
     if ((n & 1) && tid == 0) lk[n - 1] = lists[n - 1];
   }
   if (tid < kWave) {
-    // log-sum-exp of the chunk partials (two passes over <= 128 pairs)
-    float2 p0 = tid < n_chunks ? part_ms[(int64_t)row * n_chunks + tid] : make_float2(-INFINITY, 0.f);
-    float2 p1 = tid + kWave < n_chunks ? part_ms[(int64_t)row * n_chunks + tid + kWave]
-                                       : make_float2(-INFINITY, 0.f);
-    const float M = wave_max_f(fmaxf(p0.x, p1.x));
+    // log-sum-exp of the chunk partials (<= 256 pairs, four per lane)
+    float2 pp[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int c = tid + h * kWave;
+      pp[h] = c < n_chunks ? part_ms[(int64_t)row * n_chunks + c] : make_float2(-INFINITY, 0.f);
+    }
+    const float M = wave_max_f(fmaxf(fmaxf(pp[0].x, pp[1].x), fmaxf(pp[2].x, pp[3].x)));
     float s = 0.f;
     if (M != -INFINITY) {
-      if (p0.x != -INFINITY) s += p0.y * __builtin_amdgcn_exp2f((p0.x - M) * kLog2e);
-      if (p1.x != -INFINITY) s += p1.y * __builtin_amdgcn_exp2f((p1.x - M) * kLog2e);
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        if (pp[h].x != -INFINITY) s += pp[h].y * __builtin_amdgcn_exp2f((pp[h].x - M) * kLog2e);
     }
     const float S = wave_sum_f(s);
     if (lane == 0) sm.lse = M + logf(S);
@@ -307,13 +312,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   }
   __syncthreads();
   if (tid < kWave) {
-    // exclusive scan of the <= 128 counts, two per lane
-    const int a = 2 * tid < n_chunks ? sm.cnt[2 * tid] : 0;
-    const int b = 2 * tid + 1 < n_chunks ? sm.cnt[2 * tid + 1] : 0;
-    const int inc = wave_inclusive_scan(a + b);
-    const int ex = inc - (a + b);
-    if (2 * tid < n_chunks) sm.cnt[2 * tid] = ex;
-    if (2 * tid + 1 < n_chunks) sm.cnt[2 * tid + 1] = ex + a;
+    // exclusive scan of the <= 256 counts, four consecutive per lane
+    int a[4], t = 0;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      a[h] = 4 * tid + h < n_chunks ? sm.cnt[4 * tid + h] : 0;
+      t += a[h];
+    }
+    const int inc = wave_inclusive_scan(t);
+    int ex = inc - t;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      if (4 * tid + h < n_chunks) sm.cnt[4 * tid + h] = ex;
+      ex += a[h];
+    }
     if (tid == kWave - 1) sm.cnt[n_chunks] = inc;
   }
   __syncthreads();
@@ -335,14 +347,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
       }
     }
   } else if (tid < kWave) {
-    // massive ties: k-step merge of the list heads (lane owns lists lane
-    // and lane + 64)
-    int pos[2] = {0, 0};
+    // massive ties: k-step merge of the list heads (lane owns lists lane,
+    // lane + 64, lane + 128 and lane + 192)
+    int pos[4] = {0, 0, 0, 0};
     for (int j = 0; j < k; ++j) {
       uint64_t best = 0;
       int who = -1;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 4; ++h) {
         const int c = lane + h * kWave;
         if (c < n_chunks && pos[h] < k) {
           const uint64_t hv = lk[c * k + pos[h]];
@@ -527,8 +539,8 @@ TopkPlan topk_plan(int n_rows, int vocab, int k) {
   const int cap_small = vocab / 1024 > 1 ? vocab / 1024 : 1;
   int more = want < cap_small ? want : cap_small;
   if (more > n_chunks) n_chunks = more;
-  if (n_chunks > kMergeMaxLists) n_chunks = kMergeMaxLists;
-  if (n_chunks > kMergeMaxKeys / k) n_chunks = kMergeMaxKeys / k;
+  if (n_chunks > kTopkPlanMaxLists) n_chunks = kTopkPlanMaxLists;
+  if (n_chunks > 8192 / k) n_chunks = 8192 / k;
   int chunk_len = (vocab + n_chunks - 1) / n_chunks;
   chunk_len = (chunk_len + 3) & ~3;
   n_chunks = (vocab + chunk_len - 1) / chunk_len;
@@ -545,8 +557,8 @@ size_t topk_workspace_bytes(int n_rows, int vocab, int k) {
 
 bool topk_supported(int n_rows, int vocab, int k) {
   const TopkPlan p = topk_plan(n_rows, vocab, k);
-  return n_rows <= 65535 && p.chunk_len <= kTopkMaxChunk && p.n_chunks <= kMergeMaxLists &&
-         p.n_chunks * k <= kMergeMaxKeys;
+  return n_rows <= 65535 && p.chunk_len <= kTopkMaxChunk && p.n_chunks <= kTopkPlanMaxLists &&
+         p.n_chunks * k <= 8192;
 }
 
 hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, int k,
@@ -559,13 +571,21 @@ hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, i
   hipLaunchKernelGGL(topk_partial_kernel, dim3(p.n_chunks, n_rows), dim3(kTopkThreads), 0,
                      stream, logits, ld, vocab, k, inv_t, p.chunk_len, p.n_chunks, part_key,
                      part_ms);
-  const int n = p.n_chunks * k;
-  const int ns = p.n_chunks * ((k + p.n_chunks - 1) / p.n_chunks);
-  if (n <= 64 * 32 && ns <= kWave) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_merge(part_key, part_ms, n_rows, p.n_chunks, k, ids, logp, lse, stream);
+}
+
+hipError_t launch_topk_merge(const uint64_t* part_key, const float2* part_ms, int n_rows,
+                             int n_chunks, int k, int32_t* ids, float* logp, float* lse,
+                             hipStream_t stream) {
+  const int n = n_chunks * k;
+  const int ns = n_chunks * ((k + n_chunks - 1) / n_chunks);
+  if (n <= 64 * 32 && ns <= kWave && n_chunks <= 2 * kWave) {
     const dim3 grid((n_rows + kWaves - 1) / kWaves);
 #define DDT_MERGE_WAVE(RR)                                                                    \
   hipLaunchKernelGGL(topk_merge_wave_kernel<RR>, grid, dim3(kTopkThreads), 0, stream, part_key, \
-                     part_ms, n_rows, p.n_chunks, k, ids, logp, lse)
+                     part_ms, n_rows, n_chunks, k, ids, logp, lse)
     if (n <= 64 * 4) DDT_MERGE_WAVE(4);
     else if (n <= 64 * 8) DDT_MERGE_WAVE(8);
     else if (n <= 64 * 16) DDT_MERGE_WAVE(16);
@@ -578,7 +598,7 @@ hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, i
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(topk_merge_kernel),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   hipLaunchKernelGGL(topk_merge_kernel, dim3(n_rows), dim3(kTopkThreads), smem, stream, part_key,
-                     part_ms, p.n_chunks, k, ids, logp, lse);
+                     part_ms, n_chunks, k, ids, logp, lse);
   return hipGetLastError();
 }
 

@@ -31,6 +31,8 @@ SIGNATURES = {
     "ddt_status_string": (_c.c_char_p, [_I]),
     "ddt_topk_logprobs_workspace_size": (_SZ, [_I, _I, _I]),
     "ddt_topk_logprobs": (_I, [_P, _I64, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
+    "ddt_lmhead_topk_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "ddt_lmhead_topk": (_I, [_P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "ddt_argmax_workspace_size": (_SZ, [_I, _I]),
     "ddt_argmax": (_I, [_P, _I64, _I, _I, _P, _P, _P, _SZ, _P]),
     "ddt_build_tree_workspace_size": (_SZ, [_I, _I, _I, _I]),
@@ -132,6 +134,37 @@ def topk_logprobs(logits: torch.Tensor, k: int, inv_temperature: float = 1.0, *,
     st = lib.ddt_topk_logprobs(_ptr(logits), ld, rows, vocab, k, float(inv_temperature),
                                _ptr(ids), _ptr(logp), _ptr(lse), _ptr(ws), wsb, _stream(stream))
     _check("ddt_topk_logprobs", st)
+    return ids, logp, lse
+
+
+# ---------------------------------------------------------------- fused LM head
+def lmhead_topk_workspace_size(n_rows: int, hidden: int, vocab: int, k: int) -> int:
+    return int(load().ddt_lmhead_topk_workspace_size(n_rows, hidden, vocab, k))
+
+
+def lmhead_topk(hidden_states: torch.Tensor, weight: torch.Tensor, k: int,
+                inv_temperature: float = 1.0, *, ids=None, logp=None, lse=None, workspace=None,
+                want_lse: bool = True, stream=None):
+    """Top-k ids / log-probs of softmax(inv_temperature * hidden_states . weight^T)
+    per row, without materialising the logits.  hidden_states bf16 [rows, hidden],
+    weight bf16 [vocab, hidden] (the LM head), both contiguous on the device."""
+    lib = load()
+    _need(hidden_states, torch.bfloat16, "hidden_states")
+    _need(weight, torch.bfloat16, "weight")
+    if hidden_states.dim() != 2 or weight.dim() != 2 or hidden_states.shape[1] != weight.shape[1]:
+        raise ValueError("need hidden_states [rows, hidden] and weight [vocab, hidden]")
+    rows, hidden = hidden_states.shape
+    vocab = weight.shape[0]
+    dev = hidden_states.device
+    ids = torch.empty(rows, k, dtype=torch.int32, device=dev) if ids is None else ids
+    logp = torch.empty(rows, k, dtype=torch.float32, device=dev) if logp is None else logp
+    if want_lse and lse is None:
+        lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    ws, wsb = _workspace(lmhead_topk_workspace_size(rows, hidden, vocab, k), dev, workspace)
+    st = lib.ddt_lmhead_topk(_ptr(hidden_states), _ptr(weight), rows, hidden, vocab, k,
+                             float(inv_temperature), _ptr(ids), _ptr(logp), _ptr(lse), _ptr(ws),
+                             wsb, _stream(stream))
+    _check("ddt_lmhead_topk", st)
     return ids, logp, lse
 
 

@@ -13,7 +13,8 @@
  *   4. ddt_accept_compact    greedy acceptance walk against the target's
  *                            argmax tokens + compaction of the accepted KV rows
  * and, between 3 and 4, ddt_argmax: the target's greedy token per tree slot
- * (a vocab-wide arg-max over the verify logits).
+ * (a vocab-wide arg-max over the verify logits); ddt_lmhead_topk feeds stage
+ * 1 from the drafter's hidden states through the shared LM head.
  *
  * Pages the operations come from (cited by title and section):
  *   [DDTree]  "Accelerating Speculative Decoding with Block Diffusion Draft
@@ -88,6 +89,43 @@ size_t ddt_topk_logprobs_workspace_size(int n_rows, int vocab, int k);
 int ddt_topk_logprobs(const float* logits, int64_t ld_logits, int n_rows, int vocab,
                       int k, float inv_temperature, int32_t* topk_ids, float* topk_logp,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fused LM head + log-softmax / top-K (stage 1 fed from hidden states).
+ *
+ * [DFlash] "임베딩과 출력 헤드는 공유한다" (embedding and output head are
+ * shared): the drafter's output head is the target's frozen LM head, so the
+ * per-position logits are one GEMM of the drafter's block hidden states with
+ * that weight.  This call computes them on MFMA and reduces them to the
+ * stage-1 outputs in the same pass: the logits never reach HBM.
+ *
+ * For each row r (0 <= r < n_rows):
+ *   z_v   = sum_h hidden_states[r, h] * weight[v, h]   (bf16 products, fp32
+ *           accumulation; the summation order is the kernel's)
+ *   x_v   = fl32(z_v * inv_temperature)
+ *   then exactly the ddt_topk_logprobs definition on x: lse, the k largest
+ *   x (ties to the smaller id), logp = x - lse.
+ *
+ * hidden_states bf16 [n_rows, hidden]   weight bf16 [vocab, hidden] (row v =
+ *   the output embedding of token v); both 16-byte aligned.
+ * topk_ids i32 [n_rows, k], topk_logp f32 [n_rows, k], lse f32 [n_rows]
+ *   (may be NULL).
+ * workspace: ddt_lmhead_topk_workspace_size() bytes (chunk partials); its
+ *   contents on entry are ignored.  The weight is read once per block of 16
+ *   rows, so the call is meant for the drafter's few block rows.
+ * Errors: EINVAL if n_rows < 1, hidden < 1, vocab < 1, k < 1, k > vocab, a
+ *         required pointer is NULL or misaligned, or inv_temperature is not
+ *         a positive finite number; EUNSUPPORTED if hidden is not a
+ *         multiple of 256 or exceeds 4096, k > 64, or the vocabulary needs
+ *         more than 256 chunks of 640 (vocab > 163840) or
+ *         chunks * k > 16384; EWORKSPACE if the workspace is too small.
+ * Preconditions (device): finite inputs.
+ * ---------------------------------------------------------------------- */
+size_t ddt_lmhead_topk_workspace_size(int n_rows, int hidden, int vocab, int k);
+int ddt_lmhead_topk(const void* hidden_states, const void* weight, int n_rows, int hidden,
+                    int vocab, int k, float inv_temperature, int32_t* topk_ids,
+                    float* topk_logp, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* ------------------------------------------------------------------------
  * Target argmax: the verifier's greedy token for every tree slot.

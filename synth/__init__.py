@@ -246,3 +246,31 @@ def make_verify_logits(seed: int, rows: int, vocab: int = QWEN3_VOCAB,
     planted = rng.integers(0, vocab, size=rows, dtype=np.int64)
     z[np.arange(rows), planted] += np.float32(peak)
     return z, planted
+
+
+def make_lmhead_case(seed: int, rows: int, hidden: int, vocab: int, delta: float = 6.0,
+                     integer: bool = False):
+    """Drafter hidden states and a shared LM head (bf16 bit patterns).
+
+    Default: H ~ N(0,1) [rows, hidden], W ~ N(0,1) * 2/sqrt(hidden)
+    [vocab, hidden] (logits of standard deviation about 2, like the logit
+    configurations), and for each row one seeded token whose weight row gets
+    delta * H[r] / |H[r]|^2 added, which raises that row's logit by about
+    delta.  integer=True draws H and W from the integers -3..3 instead (every
+    product and sum exact in float32).  Returns (h_bits [rows, hidden],
+    w_bits [vocab, hidden], planted [rows])."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if integer:
+        h = rng.integers(-3, 4, size=(rows, hidden)).astype(np.float32)
+        w = rng.integers(-3, 4, size=(vocab, hidden)).astype(np.float32)
+        planted = rng.integers(0, vocab, size=rows, dtype=np.int64)
+        return f32_to_bf16_bits(h), f32_to_bf16_bits(w), planted
+    h = rng.standard_normal((rows, hidden), dtype=np.float32)
+    w = rng.standard_normal((vocab, hidden), dtype=np.float32)
+    w *= np.float32(2.0 / np.sqrt(hidden))
+    planted = rng.integers(0, vocab, size=rows, dtype=np.int64)
+    h_b = f32_to_bf16_bits(h)
+    hr = bf16_bits_to_f32(h_b)
+    for r in range(rows):
+        w[planted[r]] += np.float32(delta) * hr[r] / np.float32(np.dot(hr[r], hr[r]))
+    return h_b, f32_to_bf16_bits(w), planted

@@ -29,7 +29,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 13
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(ddt.SIGNATURES)
@@ -62,6 +62,31 @@ def test_topk_validation(lib):
 
 def test_topk_rows_beyond_grid_limit(lib):
     assert _topk(lib, rows=65536) == ddt.DDT_EUNSUPPORTED
+
+
+def _lmhead(lib, hs=FAKE, w=FAKE, rows=16, hidden=4096, V=151936, k=32, inv_t=1.0, ids=FAKE,
+            logp=FAKE, ws=FAKE, wsb=1 << 30):
+    return lib.ddt_lmhead_topk(hs, w, rows, hidden, V, k, inv_t, ids, logp, None, ws, wsb, None)
+
+
+def test_lmhead_validation(lib):
+    E = ddt
+    assert _lmhead(lib, hs=None) == E.DDT_EINVAL
+    assert _lmhead(lib, w=None) == E.DDT_EINVAL
+    assert _lmhead(lib, ids=None) == E.DDT_EINVAL
+    assert _lmhead(lib, rows=0) == E.DDT_EINVAL
+    assert _lmhead(lib, k=0) == E.DDT_EINVAL
+    assert _lmhead(lib, inv_t=-1.0) == E.DDT_EINVAL
+    assert _lmhead(lib, w=ctypes.c_void_p(264)) == E.DDT_EINVAL      # misaligned
+    assert _lmhead(lib, hidden=4096 + 256) == E.DDT_EUNSUPPORTED
+    assert _lmhead(lib, hidden=1000) == E.DDT_EUNSUPPORTED
+    assert _lmhead(lib, k=65) == E.DDT_EUNSUPPORTED
+    assert _lmhead(lib, V=640 * 256 + 1) == E.DDT_EUNSUPPORTED       # > 256 chunks
+    assert _lmhead(lib, ws=None) == E.DDT_EWORKSPACE
+    need = lib.ddt_lmhead_topk_workspace_size(16, 4096, 151936, 32)
+    assert need > 16 * 238 * 32 * 8                                  # 238 chunks of 640
+    assert _lmhead(lib, wsb=need - 1) == E.DDT_EWORKSPACE
+    assert lib.ddt_lmhead_topk_workspace_size(16, 1000, 151936, 32) == 0
 
 
 def _argmax(lib, logits=FAKE, ld=151936, rows=257, V=151936, ids=FAKE, maxv=None, ws=FAKE,
