@@ -171,6 +171,29 @@ def stream_passes(args, torch, ddt, synth, dev):
     return out, c5out, lmout
 
 
+def tree_rope_leg(torch, ddt, steps, cfg, dev):
+    """Tree positions + rotary embedding + tree K/V scatter (the step between
+    the tree build and verify attention) on each input set's own tree: q, k
+    and v of the verify rows, written to a separate cache, 20 sets per graph."""
+    P, N = cfg.prefix[0], cfg.B + 1
+    calls = []
+    for s in steps:
+        q = s.vq.clone()
+        kn = s.vk[P:P + N].clone().view(1, N, cfg.hkv, cfg.D)
+        vn = s.vv[P:P + N].clone().view(1, N, cfg.hkv, cfg.D)
+        kc = torch.zeros(P + N, cfg.hkv, cfg.D, dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros_like(kc)
+        pos = torch.empty(1, N, dtype=torch.int32, device=dev)
+        calls.append(lambda s=s, q=q, kn=kn, vn=vn, kc=kc, vc=vc, pos=pos: ddt.tree_rope_kv(
+            s.tree["depth"], s.tree["n_nodes"], s.prefix, s.kv_base, q, kn, vn, kc, vc, 1.0e6,
+            positions=pos))
+    t = time_graph(torch, calls, 50)
+    nb = (N * cfg.hq * cfg.D * 2 * 2 + 2 * N * cfg.hkv * cfg.D * 2 * 2 + N * 4 * 2)
+    return {"rows": N, "hq": cfg.hq, "hkv": cfg.hkv, "D": cfg.D, "algorithmic_bytes": nb,
+            "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", "us": round(t * 1e6, 3),
+            "achieved": round(nb / t / 1e9, 1), "frac": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def log(args, msg):
     if not args.quiet:
         print(msg, file=sys.stderr, flush=True)
@@ -436,6 +459,7 @@ def main():
         },
     }
 
+    result["tree_rope_kv"] = tree_rope_leg(torch, ddt, steps, cfg, dev)
     if not args.no_streams:
         (result["target_argmax"], result["logit_pass_512rows"],
          result["lmhead_topk"]) = stream_passes(args, torch, ddt, synth, dev)

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libddt.so")
-SOURCES = ["api.hip", "topk.hip", "argmax.hip", "lmhead.hip", "tree.hip", "attention.hip", "accept.hip"]
+SOURCES = ["api.hip", "topk.hip", "argmax.hip", "lmhead.hip", "rope.hip", "tree.hip", "attention.hip", "accept.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

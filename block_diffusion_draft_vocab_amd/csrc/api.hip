@@ -90,6 +90,30 @@ DDT_EXPORT int ddt_lmhead_topk(const void* hidden_states, const void* weight, in
                                                workspace, static_cast<hipStream_t>(stream)));
 }
 
+// ---- tree positions + RoPE + K/V scatter ------------------------------------
+DDT_EXPORT int ddt_tree_rope_kv(const int32_t* node_depth, const int32_t* n_nodes, int batch,
+                                int n_max, const int32_t* prefix_len, const int64_t* kv_base,
+                                void* q, const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, int hq, int hkv, int head_dim, float rope_base,
+                                int32_t* positions, void* stream) {
+  if (batch < 1 || n_max < 1 || hq < 1 || hkv < 1) return DDT_EINVAL;
+  if (node_depth == nullptr || n_nodes == nullptr || prefix_len == nullptr ||
+      kv_base == nullptr || q == nullptr || k_new == nullptr || v_new == nullptr ||
+      k_cache == nullptr || v_cache == nullptr)
+    return DDT_EINVAL;
+  if (!(rope_base > 1.f) || !isfinite(rope_base)) return DDT_EINVAL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return DDT_EINVAL;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return DDT_EUNSUPPORTED;
+  if (batch > 65535) return DDT_EUNSUPPORTED;
+  return launch_status(ddt::launch_tree_rope_kv(node_depth, n_nodes, batch, n_max, prefix_len,
+                                                kv_base, q, k_new, v_new, k_cache, v_cache, hq,
+                                                hkv, head_dim, rope_base, positions,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 // ---- target argmax --------------------------------------------------------
 DDT_EXPORT size_t ddt_argmax_workspace_size(int n_rows, int vocab) {
   if (n_rows < 1 || vocab < 1) return 0;

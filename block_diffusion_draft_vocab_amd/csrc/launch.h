@@ -44,6 +44,15 @@ hipError_t launch_lmhead_topk(const void* hs, const void* w, int n_rows, int hid
                               int k, float inv_t, int32_t* ids, float* logp, float* lse,
                               void* ws, hipStream_t stream);
 
+// ---- tree positions + rotary embedding + tree K/V scatter -------------------
+constexpr int kRopeThreads = 256;
+constexpr int kRopeMaxD = 256;
+hipError_t launch_tree_rope_kv(const int32_t* depth, const int32_t* n_nodes, int batch, int n_max,
+                               const int32_t* prefix_len, const int64_t* kv_base, void* q,
+                               const void* k_new, const void* v_new, void* k_cache,
+                               void* v_cache, int hq, int hkv, int head_dim, float rope_base,
+                               int32_t* positions, hipStream_t stream);
+
 // ---- target argmax (the verifier's greedy tokens) ------------------------
 struct ArgmaxPlan {
   int n_chunks;

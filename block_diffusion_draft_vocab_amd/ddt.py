@@ -33,6 +33,8 @@ SIGNATURES = {
     "ddt_topk_logprobs": (_I, [_P, _I64, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "ddt_lmhead_topk_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "ddt_lmhead_topk": (_I, [_P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
+    "ddt_tree_rope_kv": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P,
+                              _P]),
     "ddt_argmax_workspace_size": (_SZ, [_I, _I]),
     "ddt_argmax": (_I, [_P, _I64, _I, _I, _P, _P, _P, _SZ, _P]),
     "ddt_build_tree_workspace_size": (_SZ, [_I, _I, _I, _I]),
@@ -166,6 +168,39 @@ def lmhead_topk(hidden_states: torch.Tensor, weight: torch.Tensor, k: int,
                              wsb, _stream(stream))
     _check("ddt_lmhead_topk", st)
     return ids, logp, lse
+
+
+# ---------------------------------------------------------------- tree RoPE + KV
+def tree_rope_kv(node_depth: torch.Tensor, n_nodes: torch.Tensor, prefix_len: torch.Tensor,
+                 kv_base: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                 v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 rope_base: float = 1.0e6, *, positions=None, want_positions: bool = True,
+                 stream=None):
+    """Positions P + depth for the tree slots, rotary embedding of q (in place)
+    and of the new k, and the scatter of k / v into the cache rows P + slot.
+    Returns positions i32 [batch, n_max] (or None)."""
+    lib = load()
+    _need(node_depth, torch.int32, "node_depth")
+    _need(n_nodes, torch.int32, "n_nodes")
+    _need(prefix_len, torch.int32, "prefix_len")
+    _need(kv_base, torch.int64, "kv_base")
+    for t, nm in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"),
+                  (v_cache, "v_cache")):
+        _need(t, torch.bfloat16, nm)
+    batch, n_max, hq, D = q.shape
+    hkv = k_new.shape[2]
+    if tuple(k_new.shape) != (batch, n_max, hkv, D) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k_new / v_new must be [batch, n_max, hkv, D]")
+    if k_cache.shape[-2:] != (hkv, D) or v_cache.shape[-2:] != (hkv, D):
+        raise ValueError("caches must be [rows, hkv, D]")
+    if want_positions and positions is None:
+        positions = torch.empty(batch, n_max, dtype=torch.int32, device=q.device)
+    st = lib.ddt_tree_rope_kv(_ptr(node_depth), _ptr(n_nodes), batch, n_max, _ptr(prefix_len),
+                              _ptr(kv_base), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                              _ptr(v_cache), hq, hkv, D, float(rope_base), _ptr(positions),
+                              _stream(stream))
+    _check("ddt_tree_rope_kv", st)
+    return positions
 
 
 # ---------------------------------------------------------------- target argmax

@@ -128,6 +128,45 @@ int ddt_lmhead_topk(const void* hidden_states, const void* weight, int n_rows, i
                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * Tree positions + rotary embedding + tree K/V scatter (between stages 2
+ * and 3b, one layer per call).
+ *
+ * [DDTree] "방법론 자세히 보기" (method in detail): the flattened tree is
+ * verified in one target pass, each token continuing the sequence after its
+ * own ancestors.  So the token in slot i sits at position P + depth[i] (the
+ * root, the bonus token, at P), not at P + i; a chain gives the ordinary
+ * positions.  The pages do not name the positional encoding; this call
+ * applies the rotary one in its common split-half form:
+ *   theta_j = rope_base^(-2j/D), a = pos * theta_j  (j < D/2)
+ *   (x_j, x_{j+D/2}) -> (x_j cos a - x_{j+D/2} sin a,
+ *                        x_{j+D/2} cos a + x_j sin a)
+ * evaluated in double precision and rounded to float, then to bf16 (both
+ * round to nearest even).
+ *
+ * For request b and slot i < n_nodes[b] (P = prefix_len[b]):
+ *   positions[b, i] = P + node_depth[b, i]     (-1 for slots >= n_nodes)
+ *   q[b, i, h, :]   rotated in place           (every q head h < hq)
+ *   k_cache[kv_base[b] + P + i, g, :] = rotate(k_new[b, i, g, :])
+ *   v_cache[kv_base[b] + P + i, g, :] = v_new[b, i, g, :]
+ * Slots >= n_nodes[b] are not read or written (q rows stay as they are).
+ *
+ * node_depth i32 [batch, n_max]; n_nodes, prefix_len i32 [batch];
+ * kv_base i64 [batch]; q bf16 [batch, n_max, hq, D]; k_new, v_new bf16
+ * [batch, n_max, hkv, D]; k_cache, v_cache bf16 [rows, hkv, D];
+ * positions i32 [batch, n_max] or NULL.  Tensors 16-byte aligned.
+ * Errors: EINVAL if batch < 1, n_max < 1, hq < 1, hkv < 1, a required
+ *         pointer is NULL or misaligned, or rope_base is not a finite
+ *         number > 1; EUNSUPPORTED if head_dim is not 32, 64, 128 or 256 or
+ *         batch > 65535.
+ * Preconditions (device): cache rows kv_base[b] + P .. + n_nodes[b] - 1
+ *   exist; n_nodes[b] <= n_max.
+ * ---------------------------------------------------------------------- */
+int ddt_tree_rope_kv(const int32_t* node_depth, const int32_t* n_nodes, int batch, int n_max,
+                     const int32_t* prefix_len, const int64_t* kv_base, void* q,
+                     const void* k_new, const void* v_new, void* k_cache, void* v_cache, int hq,
+                     int hkv, int head_dim, float rope_base, int32_t* positions, void* stream);
+
+/* ------------------------------------------------------------------------
  * Target argmax: the verifier's greedy token for every tree slot.
  *
  * [DDTree] "방법론 자세히 보기" (method in detail): the target model runs once

@@ -29,7 +29,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(ddt.SIGNATURES)
@@ -87,6 +87,24 @@ def test_lmhead_validation(lib):
     assert need > 16 * 238 * 32 * 8                                  # 238 chunks of 640
     assert _lmhead(lib, wsb=need - 1) == E.DDT_EWORKSPACE
     assert lib.ddt_lmhead_topk_workspace_size(16, 1000, 151936, 32) == 0
+
+
+def _rope(lib, depth=FAKE, q=FAKE, kc=FAKE, batch=1, n_max=257, hq=32, hkv=8, D=128, base=1e6):
+    return lib.ddt_tree_rope_kv(depth, FAKE, batch, n_max, FAKE, FAKE, q, FAKE, FAKE, kc, FAKE,
+                                hq, hkv, D, base, None, None)
+
+
+def test_tree_rope_validation(lib):
+    E = ddt
+    assert _rope(lib, depth=None) == E.DDT_EINVAL
+    assert _rope(lib, q=None) == E.DDT_EINVAL
+    assert _rope(lib, kc=ctypes.c_void_p(264)) == E.DDT_EINVAL      # misaligned
+    assert _rope(lib, batch=0) == E.DDT_EINVAL
+    assert _rope(lib, n_max=0) == E.DDT_EINVAL
+    assert _rope(lib, base=1.0) == E.DDT_EINVAL
+    assert _rope(lib, base=float("nan")) == E.DDT_EINVAL
+    assert _rope(lib, D=96) == E.DDT_EUNSUPPORTED
+    assert _rope(lib, batch=65536) == E.DDT_EUNSUPPORTED
 
 
 def _argmax(lib, logits=FAKE, ld=151936, rows=257, V=151936, ids=FAKE, maxv=None, ws=FAKE,
