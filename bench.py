@@ -194,6 +194,33 @@ def tree_rope_leg(torch, ddt, steps, cfg, dev):
             "achieved": round(nb / t / 1e9, 1), "frac": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def packed_blocks_leg(torch, ddt, steps, cfg, dev):
+    """Packed drafter blocks: 4 blocks of 16 query rows over the 2048-row
+    context plus their own rows (block-diagonal), drafter head shape 32/8/128,
+    from each set's verify tensors (the first 64 query rows and cache rows);
+    20 calls per graph."""
+    P, nb, L = cfg.drafter_ctx, 4, cfg.L
+    n = nb * L
+    desc = ddt.attn_desc(1, cfg.hq, cfg.hkv, cfg.D, n, P + n)
+    ws = torch.empty(max(1, ddt.attention_workspace_size(desc)), dtype=torch.uint8, device=dev)
+    base = torch.zeros(1, dtype=torch.int64, device=dev)
+    pre = torch.full((1,), P, dtype=torch.int32, device=dev)
+    nq = torch.full((1,), n, dtype=torch.int32, device=dev)
+    calls = []
+    for s in steps:
+        q = s.vq[:, :n].contiguous()
+        out = torch.empty_like(q)
+        calls.append(lambda s=s, q=q, out=out: ddt.masked_attention(
+            q, s.vk, s.vv, base, pre, nq, None, max_kv_len=P + n, out=out, workspace=ws,
+            block_len=L))
+    t = time_graph(torch, calls, 50)
+    nb_bytes = (P + n) * cfg.hkv * cfg.D * 2 * 2 + 2 * n * cfg.hq * cfg.D * 2
+    return {"blocks": nb, "block_len": L, "context": P, "algorithmic_bytes": nb_bytes,
+            "bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", "us": round(t * 1e6, 3),
+            "achieved": round(nb_bytes / t / 1e9, 1),
+            "frac": round(nb_bytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def log(args, msg):
     if not args.quiet:
         print(msg, file=sys.stderr, flush=True)
@@ -460,6 +487,7 @@ def main():
     }
 
     result["tree_rope_kv"] = tree_rope_leg(torch, ddt, steps, cfg, dev)
+    result["packed_blocks_attn"] = packed_blocks_leg(torch, ddt, steps, cfg, dev)
     if not args.no_streams:
         (result["target_argmax"], result["logit_pass_512rows"],
          result["lmhead_topk"]) = stream_passes(args, torch, ddt, synth, dev)

@@ -204,8 +204,31 @@ DDT_EXPORT int ddt_masked_attention(const ddt_attn_desc* desc, const void* q, co
   const float scale = desc->scale > 0.f ? desc->scale : 1.0f / sqrtf((float)desc->head_dim);
   return launch_status(ddt::launch_attention(
       desc->batch, desc->hq, desc->hkv, desc->head_dim, desc->n_q_max, desc->mask_words,
-      desc->max_kv_len, scale, q, k_cache, v_cache, kv_base, prefix_len, n_q, own_mask, out,
+      desc->max_kv_len, scale, q, k_cache, v_cache, kv_base, prefix_len, n_q, own_mask, 0, out,
       lse_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+DDT_EXPORT int ddt_packed_block_attention(const ddt_attn_desc* desc, int block_len, const void* q,
+                                          const void* k_cache, const void* v_cache,
+                                          const int64_t* kv_base, const int32_t* prefix_len,
+                                          const int32_t* n_q, void* out, float* lse_out,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = attn_desc_check(desc, false);
+  if (st != DDT_OK) return st;
+  if (block_len < 1) return DDT_EINVAL;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || kv_base == nullptr ||
+      prefix_len == nullptr || n_q == nullptr || out == nullptr)
+    return DDT_EINVAL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return DDT_EINVAL;
+  const size_t need = ddt::attn_workspace_bytes(desc->batch, desc->hq, desc->hkv,
+                                                desc->head_dim, desc->n_q_max, desc->max_kv_len);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return DDT_EWORKSPACE;
+  const float scale = desc->scale > 0.f ? desc->scale : 1.0f / sqrtf((float)desc->head_dim);
+  return launch_status(ddt::launch_attention(
+      desc->batch, desc->hq, desc->hkv, desc->head_dim, desc->n_q_max, 0, desc->max_kv_len, scale,
+      q, k_cache, v_cache, kv_base, prefix_len, n_q, nullptr, block_len, out, lse_out, workspace,
+      static_cast<hipStream_t>(stream)));
 }
 
 // ---- stage 4 ---------------------------------------------------------------

@@ -60,6 +60,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kMaxTilesPerSplit = 16;
+constexpr int kMinTilesPerSplit = 3;  // measured: 2 and 4 were slower for one 256-column group
 constexpr int kCUs = 256;
 
 template <int D>
@@ -100,6 +101,8 @@ struct Params {
   int n_cg_full;      // column groups with all 8 waves busy at n_q_max
   int n_split;        // key splits of those groups
   int n_split_tail;   // key splits of the trailing partial group (0: none)
+  int block_len;      // > 0: own rows form blocks of this many rows, each query
+                      // sees only its own block's rows (packed drafter blocks)
   float scale_log2;
 };
 
@@ -127,15 +130,16 @@ __device__ __forceinline__ void mask_words_for(const uint64_t* mrow, int W, int 
 }
 
 // Which of the 64 keys [key0, key0+64) a column may see: all prefix keys,
-// and own keys j in [0, nq) that its mask row allows (all of them without a
-// mask).  lo/hi come from mask_words_for(key0 - P); key0 + 64 > P - 64.
-__device__ __forceinline__ uint64_t visible64(int key0, int P, int nq, bool has_mask,
-                                              uint64_t lo, uint64_t hi) {
+// and own keys j in [own_lo, own_hi) that its mask row allows (all of them
+// without a mask).  lo/hi come from mask_words_for(key0 - P); key0 + 64 > P - 64.
+__device__ __forceinline__ uint64_t visible64(int key0, int P, int own_lo, int own_hi,
+                                              bool has_mask, uint64_t lo, uint64_t hi) {
   if (key0 + kKT <= P) return ~0ull;
   const uint64_t pre = key0 >= P ? 0ull : ((1ull << (P - key0)) - 1ull);
   const int j0 = key0 - P;
-  const int b_lo = j0 < 0 ? -j0 : 0;
-  int b_hi = nq - j0;
+  int b_lo = own_lo - j0;
+  b_lo = b_lo < 0 ? 0 : b_lo;
+  int b_hi = own_hi - j0;
   b_hi = b_hi > 64 ? 64 : b_hi;
   uint64_t range = 0ull;
   if (b_hi > b_lo)
@@ -294,6 +298,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const uint64_t* mrow =
       has_mask ? p.mask + ((int64_t)r * p.n_q_max + qi) * p.mask_words : nullptr;
   const bool lane_mask = has_mask && valid;
+  // own rows this column may see: all nq, or its packed block
+  const int own_lo = p.block_len > 0 ? (qi / p.block_len) * p.block_len : 0;
+  const int own_hi = p.block_len > 0 ? min(nq, own_lo + p.block_len) : nq;
 
   // ---- staging: copy j of this thread moves 16-byte chunk
   // L = (8 j + wid) * 64 + lane of the (K tile | V tile) pair; a wave's 64
@@ -371,7 +378,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     for (int i = 0; i < kMaxTilesPerSplit; ++i) {
       const int key0 = (t_begin + i) * kKT;
       if (i >= nt_range || key0 + kKT <= P) continue;
-      const uint64_t w = valid ? visible64(key0, P, nq, has_mask, wlo[i], whi[i]) : 0ull;
+      const uint64_t w =
+          valid ? visible64(key0, P, own_lo, own_hi, has_mask, wlo[i], whi[i]) : 0ull;
       if (h2 == 0) win_lds[i][wid * kColsPerWave + n] = w;
       if (wave_active && __ballot(w != 0ull) != 0 && lane == 0) atomicOr(&own_need[i], 1u);
     }
@@ -737,6 +745,10 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int n_q_max, int max_kv_len) {
   plan.n_cg_full = n_cg_full;
   if (heavy > 0) {
     long s = kCUs / heavy;
+    // at least kMinTilesPerSplit tiles per split: a split of one or two
+    // tiles costs more in partial stores and merge reads than it saves
+    const long by_tiles = max_tiles / kMinTilesPerSplit;
+    if (s > by_tiles) s = by_tiles;
     while (s > 1 && heavy * s + tail * tail_split((int)s) > kCUs) --s;
     plan.n_split = clamp_split(s);
     plan.n_split_tail = tail_split(plan.n_split);
@@ -762,7 +774,7 @@ hipError_t launch_attention(int batch, int hq, int hkv, int head_dim, int n_q_ma
                             int mask_words, int max_kv_len, float scale, const void* q,
                             const void* k, const void* v, const int64_t* kv_base,
                             const int32_t* prefix_len, const int32_t* n_q,
-                            const uint64_t* mask, void* out, float* lse, void* ws,
+                            const uint64_t* mask, int block_len, void* out, float* lse, void* ws,
                             hipStream_t stream) {
   const AttnPlan plan = attn_plan(batch, hq, hkv, n_q_max, max_kv_len);
   Params prm;
@@ -789,6 +801,7 @@ hipError_t launch_attention(int batch, int hq, int hkv, int head_dim, int n_q_ma
   prm.n_cg_full = plan.n_cg_full;
   prm.n_split = plan.n_split;
   prm.n_split_tail = plan.n_split_tail;
+  prm.block_len = block_len;
   prm.scale_log2 = scale * kLog2e;
   switch (head_dim) {
     case 32: return launch_d<32>(prm, plan, stream);

@@ -87,7 +87,7 @@ hipError_t launch_attention(int batch, int hq, int hkv, int head_dim, int n_q_ma
                             int mask_words, int max_kv_len, float scale, const void* q,
                             const void* k, const void* v, const int64_t* kv_base,
                             const int32_t* prefix_len, const int32_t* n_q,
-                            const uint64_t* mask, void* out, float* lse, void* ws,
+                            const uint64_t* mask, int block_len, void* out, float* lse, void* ws,
                             hipStream_t stream);
 
 // ---- stage 4 --------------------------------------------------------------

@@ -41,6 +41,7 @@ SIGNATURES = {
     "ddt_build_tree": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "ddt_masked_attention_workspace_size": (_SZ, [_P]),
     "ddt_masked_attention": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "ddt_packed_block_attention": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "ddt_accept_compact": (_I, [_P, _P, _P, _I, _P, _I, _I, _P, _P, _P, _P, _I, _I64, _I, _I,
                                 _P, _P, _P, _P, _P]),
 }
@@ -274,9 +275,11 @@ def masked_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                      kv_base: torch.Tensor, prefix_len: torch.Tensor, n_q: torch.Tensor,
                      own_mask: Optional[torch.Tensor] = None, *, max_kv_len: int,
                      scale: float = 0.0, out=None, lse=None, want_lse=False, workspace=None,
-                     stream=None):
+                     block_len: int = 0, stream=None):
     """q bf16 [b, n_q_max, hq, D]; k/v bf16 [rows, hkv, D]; own_mask int64
-    [b, n_q_max, W] (bit patterns) or None for the dense drafter block."""
+    [b, n_q_max, W] (bit patterns) or None for the dense drafter block.
+    block_len > 0 (no mask): packed drafter blocks, each query sees the prefix
+    and only its own block of block_len own rows."""
     lib = load()
     _need(q, torch.bfloat16, "q")
     _need(k_cache, torch.bfloat16, "k_cache")
@@ -295,6 +298,15 @@ def masked_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     if want_lse and lse is None:
         lse = torch.empty(b, n_q_max, hq, dtype=torch.float32, device=q.device)
     ws, wsb = _workspace(attention_workspace_size(desc), q.device, workspace)
+    if block_len:
+        if own_mask is not None:
+            raise ValueError("block_len and own_mask are exclusive")
+        st = lib.ddt_packed_block_attention(ctypes.byref(desc), int(block_len), _ptr(q),
+                                            _ptr(k_cache), _ptr(v_cache), _ptr(kv_base),
+                                            _ptr(prefix_len), _ptr(n_q), _ptr(out), _ptr(lse),
+                                            _ptr(ws), wsb, _stream(stream))
+        _check("ddt_packed_block_attention", st)
+        return (out, lse) if want_lse else out
     st = lib.ddt_masked_attention(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(kv_base), _ptr(prefix_len), _ptr(n_q), _ptr(own_mask),
                                   _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(stream))

@@ -298,6 +298,26 @@ int ddt_masked_attention(const ddt_attn_desc* desc, const void* q, const void* k
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Stage 3, packed drafter blocks: block-diagonal own-row visibility.
+ *
+ * [DFlash] "여러 블록을 한 번에 학습하되, 블록끼리 새지 않게 막는다"
+ * (several blocks are processed in one sequence, kept from leaking into one
+ * another): the drafter's attention mask lets rows of one block see each
+ * other but no row of another block.  Here the own rows of request r are
+ * cut into consecutive blocks of block_len rows (the last one may be
+ * shorter); query i sees every prefix (context) row and the own rows j with
+ * j / block_len == i / block_len.  Everything else -- layouts, arithmetic,
+ * outputs, workspace (ddt_masked_attention_workspace_size) -- is exactly
+ * ddt_masked_attention in drafter mode, which block_len >= n_q reproduces.
+ * Errors: those of ddt_masked_attention, plus EINVAL if block_len < 1.
+ * ---------------------------------------------------------------------- */
+int ddt_packed_block_attention(const ddt_attn_desc* desc, int block_len, const void* q,
+                               const void* k_cache, const void* v_cache, const int64_t* kv_base,
+                               const int32_t* prefix_len, const int32_t* n_q, void* out,
+                               float* lse_out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------------
  * Stage 4: greedy acceptance walk + KV compaction.
  *
  * [DDTree] "방법론 자세히 보기": the verifier follows the tree along the

@@ -12,6 +12,10 @@ Two visibility rules share one definition:
   key/value memory into every draft layer, and the block of masked positions
   is filled jointly, so block queries see all context rows and every row of
   their own block (no mask).
+* packed drafter blocks -- [DFlash] "여러 블록을 한 번에 학습하되, 블록끼리 새지
+  않게 막는다": several blocks share one sequence and the mask keeps them
+  apart, so own row j is visible to query i only when both lie in the same
+  block of block_len consecutive own rows (every prefix row stays visible).
 
 Readings: softmax scale 1/sqrt(D) unless given; query head h reads KV head
 floor(h / (hq/hkv)); no positional terms inside the kernel (inputs are taken as
@@ -35,9 +39,10 @@ def _mask_bits(words: np.ndarray, n: int) -> np.ndarray:
 
 
 def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_base, prefix_len,
-                     n_q, own_mask=None, scale=None):
+                     n_q, own_mask=None, scale=None, block_len=None):
     """q [b, nq_max, hq, D]; k, v [rows, hkv, D] (float values of bf16 data);
-    own_mask u64 [b, nq_max, W] or None for the dense drafter block.
+    own_mask u64 [b, nq_max, W] or None for the dense drafter block;
+    block_len (no mask): packed blocks of that many own rows.
     Returns (out f64 [b, nq_max, hq, D], lse f64 [b, nq_max, hq]); rows
     i >= n_q[r] are left at zero."""
     q = np.asarray(q, dtype=np.float64)
@@ -64,6 +69,10 @@ def masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, kv_base, prefi
         if own_mask is not None:
             for i in range(n):
                 visible[i, P:] = _mask_bits(own_mask[r, i], n)
+        elif block_len is not None:
+            for i in range(n):
+                for j in range(n):
+                    visible[i, P + j] = (i // block_len) == (j // block_len)
         for h in range(hq):
             kh = h // g
             s = (q[r, :n, h, :] @ Kr[:, kh, :].T) * scale        # [n, T]

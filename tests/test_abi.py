@@ -29,7 +29,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 15
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(ddt.SIGNATURES)
@@ -105,6 +105,18 @@ def test_tree_rope_validation(lib):
     assert _rope(lib, base=float("nan")) == E.DDT_EINVAL
     assert _rope(lib, D=96) == E.DDT_EUNSUPPORTED
     assert _rope(lib, batch=65536) == E.DDT_EUNSUPPORTED
+
+
+def test_packed_block_validation(lib):
+    d = ddt.attn_desc(1, 32, 8, 128, 64, 2048 + 64)
+    need = lib.ddt_masked_attention_workspace_size(ctypes.byref(d))
+    call = lambda bl, q=FAKE, ws=FAKE: lib.ddt_packed_block_attention(
+        ctypes.byref(d), bl, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, need, None)
+    assert call(0) == ddt.DDT_EINVAL
+    assert call(16, q=None) == ddt.DDT_EINVAL
+    assert call(16, q=ctypes.c_void_p(260)) == ddt.DDT_EINVAL
+    if need > 0:
+        assert call(16, ws=None) == ddt.DDT_EWORKSPACE
 
 
 def _argmax(lib, logits=FAKE, ld=151936, rows=257, V=151936, ids=FAKE, maxv=None, ws=FAKE,

@@ -116,3 +116,38 @@ def test_identical_visible_sets_give_identical_rows():
     dense[2, 3] = True            # row 2 sees {0, 2, 3} too
     out, _ = masked_attention(q, k, v, base, [P], [n], _pack(dense)[None])
     assert np.array_equal(out[0, 2], out[0, 3])
+
+
+@pytest.mark.parametrize("n,bl", [(64, 16), (40, 16), (7, 3)])
+def test_packed_blocks_match_sdpa_with_block_diagonal_mask(n, bl):
+    """Packed drafter blocks: SDPA with every prefix row plus the block-diagonal
+    own-row mask (the last block may be short)."""
+    P, hq, hkv, D = 96, 8, 2, 32
+    q, k, v, base = _qkv(13 + n, 1, n, P, hq, hkv, D)
+    out, _ = masked_attention(q, k, v, base, [P], [n], None, block_len=bl)
+    blk = np.arange(n) // bl
+    allowed = np.concatenate([np.ones((n, P), dtype=bool), blk[:, None] == blk[None, :]], axis=1)
+    want = _sdpa(q[0], k, v, allowed, hq // hkv)
+    assert np.abs(out[0] - want).max() < 1e-12
+
+
+def test_packed_block_at_least_n_is_the_dense_drafter_block():
+    P, n, hq, hkv, D = 64, 16, 4, 2, 32
+    q, k, v, base = _qkv(14, 1, n, P, hq, hkv, D)
+    a, la = masked_attention(q, k, v, base, [P], [n], None, block_len=n)
+    b, lb = masked_attention(q, k, v, base, [P], [n], None)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_packed_blocks_do_not_leak():
+    """Changing the own rows of one block leaves every other block's output
+    unchanged."""
+    P, n, bl, hq, hkv, D = 50, 48, 16, 4, 1, 32
+    q, k, v, base = _qkv(15, 1, n, P, hq, hkv, D)
+    a, _ = masked_attention(q, k, v, base, [P], [n], None, block_len=bl)
+    k2, v2 = k.copy(), v.copy()
+    k2[P + 16:P + 32] += 1.0
+    v2[P + 16:P + 32] -= 2.0
+    b, _ = masked_attention(q, k2, v2, base, [P], [n], None, block_len=bl)
+    assert np.array_equal(a[0, :16], b[0, :16]) and np.array_equal(a[0, 32:], b[0, 32:])
+    assert not np.array_equal(a[0, 16:32], b[0, 16:32])
