@@ -122,3 +122,34 @@ def test_attention_workspace_reuse_and_graph_replay(gpu, masked):
         g.replay()
         torch.cuda.synchronize()
         check(out, lse, case, mask)
+
+
+@pytest.mark.parametrize("masked", [True, False], ids=["verify", "drafter"])
+def test_attention_empty_splits_ignore_stale_workspace(gpu, masked):
+    """A launch planned for a long key range (max_kv_len 4096) on a request
+    that only has 100 keys leaves most key splits empty; their workspace
+    slots are never written.  Filled with 0xFF bytes (NaN partials), they
+    must not reach the result."""
+    rng = np.random.default_rng(91)
+    n, P, hq, hkv, D = 20, 80, 8, 2, 128
+    q = synth.f32_to_bf16_bits(rng.standard_normal((1, n, hq, D), dtype=np.float32))
+    k = synth.f32_to_bf16_bits(rng.standard_normal((P + n, hkv, D), dtype=np.float32))
+    v = synth.f32_to_bf16_bits(rng.standard_normal((P + n, hkv, D), dtype=np.float32))
+    mask = None
+    if masked:
+        from oracle.tree import ancestor_mask
+        parent = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, n)], np.int32)
+        mask = ancestor_mask(parent, n, n)[None]
+    desc = ddt.attn_desc(1, hq, hkv, D, n, 4096, 1 if masked else 0)
+    ws = torch.full((ddt.attention_workspace_size(desc),), 0xFF, dtype=torch.uint8, device=gpu)
+    out, lse = ddt.masked_attention(
+        dev_bf16(q, gpu), dev_bf16(k, gpu), dev_bf16(v, gpu),
+        torch.zeros(1, dtype=torch.int64, device=gpu), torch.full((1,), P, dtype=torch.int32,
+                                                                   device=gpu),
+        torch.full((1,), n, dtype=torch.int32, device=gpu),
+        None if mask is None else mask_to_dev(mask, gpu), max_kv_len=4096, want_lse=True,
+        workspace=ws)
+    torch.cuda.synchronize()
+    oo, ol = oracle_attn(bf16_f32(q), bf16_f32(k), bf16_f32(v), [0], [P], [n], mask)
+    assert np.abs(out.float().cpu().numpy()[0] - oo[0]).max() <= 2e-2
+    assert np.abs(lse.cpu().numpy()[0] - ol[0]).max() <= 2e-2
