@@ -101,6 +101,7 @@ struct Params {
   int n_cg_full;      // column groups with all 8 waves busy at n_q_max
   int n_split;        // key splits of those groups
   int n_split_tail;   // key splits of the trailing partial group (0: none)
+  int max_tiles;      // key tiles of the longest request the plan was made for
   int block_len;      // > 0: own rows form blocks of this many rows, each query
                       // sees only its own block's rows (packed drafter blocks)
   float scale_log2;
@@ -111,6 +112,14 @@ struct Params {
 __device__ __forceinline__ void split_range(int s, int n_split, int nt, int& t0, int& t1) {
   t0 = (int)((uint32_t)(s * nt) / (uint32_t)n_split);
   t1 = (int)((uint32_t)((s + 1) * nt) / (uint32_t)n_split);
+}
+// Key splits request r actually uses: the plan's count scaled by the
+// request's share of the longest key range, so that a short request in a
+// ragged batch gets splits of about the same length as the longest one
+// (never more tiles per split than the plan allows: ns >= max_tiles / 16).
+__device__ __forceinline__ int request_splits(int ns, int nt, int max_tiles) {
+  const long v = ((long)nt * ns + max_tiles - 1) / max_tiles;
+  return v < 1 ? 1 : (v > ns ? ns : (int)v);
 }
 // Split s is empty only when there are fewer tiles than splits.
 __device__ __forceinline__ bool split_nonempty(int s, int n_split, int nt) {
@@ -279,6 +288,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int col0 = cg * kColsPerWG;
   if (col0 >= ncols || T <= 0) return;
   const int ntiles = (T + kKT - 1) / kKT;
+  n_split = request_splits(n_split, ntiles, p.max_tiles);
+  if (s >= n_split) return;
   int t_begin, t_end;
   split_range(s, n_split, ntiles, t_begin, t_end);
   if (t_begin >= t_end) return;
@@ -643,8 +654,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
   if (T <= 0) return;
   const int g = p.hq / p.hkv;
   const int col = qi * g + head % g;
-  const int ns = col / kColsPerWG < p.n_cg_full ? p.n_split : p.n_split_tail;
   const int ntiles = (T + kKT - 1) / kKT;
+  const int ns = request_splits(col / kColsPerWG < p.n_cg_full ? p.n_split : p.n_split_tail,
+                                ntiles, p.max_tiles);
   const int64_t ro = (int64_t)gid * p.n_split;
   float M = -INFINITY;
   float Lsum = 0.f;
@@ -802,6 +814,7 @@ hipError_t launch_attention(int batch, int hq, int hkv, int head_dim, int n_q_ma
   prm.n_split = plan.n_split;
   prm.n_split_tail = plan.n_split_tail;
   prm.block_len = block_len;
+  prm.max_tiles = (max_kv_len + kKT - 1) / kKT;
   prm.scale_log2 = scale * kLog2e;
   switch (head_dim) {
     case 32: return launch_d<32>(prm, plan, stream);
