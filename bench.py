@@ -221,6 +221,49 @@ def packed_blocks_leg(torch, ddt, steps, cfg, dev):
             "frac": round(nb_bytes / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def serving_verify_leg(args, torch, ddt, synth, dev):
+    """Verify attention of the ragged serving batch: 32 requests, 65 tree rows
+    each, prefixes U{512..8192}, 32/4/128.  The trees come from this library's
+    own top-K and tree kernels on the batch's synthetic logits; FLOPs count
+    the keys each tree row can see."""
+    c5 = synth.CONFIGS[5]
+    N = c5.B + 1
+    sets = []
+    for i in range(2):
+        case = synth.make_case(c5, seed=args.seed + 500 + i, with_drafter=False)
+        lg = torch.from_numpy(case.logits).to(dev)
+        ids, logp, _ = ddt.topk_logprobs(lg, c5.K)
+        tree = ddt.build_tree(logp, ids, torch.from_numpy(case.root_token).to(dev), c5.batch,
+                              c5.L, c5.k_tree, c5.B)
+        torch.cuda.synchronize()
+        depth = tree["depth"].cpu().numpy()
+        nn = tree["n_nodes"].cpu().numpy()
+        vis = sum(int(nn[r]) * int(case.prefix_len[r]) + int((depth[r, :nn[r]] + 1).sum())
+                  for r in range(c5.batch))
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+        sets.append(dict(q=bf16(case.vq_bits), k=bf16(case.vk_bits), v=bf16(case.vv_bits),
+                         base=torch.from_numpy(case.kv_base).to(dev),
+                         pre=torch.from_numpy(case.prefix_len).to(dev), nq=tree["n_nodes"],
+                         mask=tree["mask"], maxkv=int(case.prefix_len.max()) + N,
+                         flops=4.0 * c5.D * c5.hq * vis))
+        del lg
+    maxkv = max(st["maxkv"] for st in sets)
+    desc = ddt.attn_desc(c5.batch, c5.hq, c5.hkv, c5.D, N, maxkv, (N + 63) // 64)
+    ws = torch.empty(max(1, ddt.attention_workspace_size(desc)), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(st["q"]) for st in sets]
+    t = time_graph(torch, [lambda st=st, o=o: ddt.masked_attention(
+        st["q"], st["k"], st["v"], st["base"], st["pre"], st["nq"], st["mask"],
+        max_kv_len=maxkv, out=o, workspace=ws) for st, o in zip(sets, outs)] * 2, 10)
+    fl = float(np.mean([st["flops"] for st in sets]))
+    return {"requests": c5.batch, "rows_per_request": N, "prefix": "U{512..8192}",
+            "hq": c5.hq, "hkv": c5.hkv, "D": c5.D, "algorithmic_flops": fl, "bound": "mfma",
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "us": round(t * 1e6, 2),
+            "achieved": round(fl / t / 1e12, 1), "frac": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
 def log(args, msg):
     if not args.quiet:
         print(msg, file=sys.stderr, flush=True)
@@ -488,6 +531,8 @@ def main():
 
     result["tree_rope_kv"] = tree_rope_leg(torch, ddt, steps, cfg, dev)
     result["packed_blocks_attn"] = packed_blocks_leg(torch, ddt, steps, cfg, dev)
+    if not args.no_streams:
+        result["verify_attn_serving"] = serving_verify_leg(args, torch, ddt, synth, dev)
     if not args.no_streams:
         (result["target_argmax"], result["logit_pass_512rows"],
          result["lmhead_topk"]) = stream_passes(args, torch, ddt, synth, dev)
