@@ -15,7 +15,8 @@
 //   The 1-D grid enumerates (KV head, request, column group, key split) with
 //   the KV head fastest: workgroups are dealt to the 8 XCDs round-robin, so
 //   with 8 KV heads all workgroups of one head share an XCD and its L2.  A
-//   trailing column group with few columns gets fewer key splits.  A second
+//   trailing column group with few columns gets fewer key splits and is
+//   enumerated beside the full groups of the same split.  A second
 //   kernel merges the splits with their log-sum-exp weights.
 //
 // Per 64-key tile
@@ -258,27 +259,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int h2 = lane >> 5;
   const int n = lane & 31;
 
-  // ---- decode the work item
+  // ---- decode the work item: (split, column group, request, KV head), KV
+  // head fastest.  The trailing partial group sits next to the full groups
+  // of the same split, so it runs while they do and finds the same K/V tiles
+  // in its XCD's L2; a group with fewer splits than the slot has exits.
   int x = blockIdx.x;
-  const int heavy = p.n_cg_full * p.batch * p.hkv * p.n_split;
-  int hk, r, cg, s, n_split;
-  if (x < heavy) {
-    hk = x % p.hkv;
-    x /= p.hkv;
-    r = x % p.batch;
-    x /= p.batch;
-    cg = x % p.n_cg_full;
-    s = x / p.n_cg_full;
-    n_split = p.n_split;
-  } else {
-    x -= heavy;
-    hk = x % p.hkv;
-    x /= p.hkv;
-    r = x % p.batch;
-    s = x / p.batch;
-    cg = p.n_cg_full;
-    n_split = p.n_split_tail;
-  }
+  const int n_groups = p.n_cg_full + (p.n_split_tail > 0 ? 1 : 0);
+  const int hk = x % p.hkv;
+  x /= p.hkv;
+  const int r = x % p.batch;
+  x /= p.batch;
+  const int cg = x % n_groups;
+  const int s = x / n_groups;
+  int n_split = cg < p.n_cg_full ? p.n_split : p.n_split_tail;
 
   const int P = p.prefix_len[r];
   const int nq = min(p.n_q[r], p.n_q_max);
@@ -707,7 +700,9 @@ bool plan_splits(const AttnPlan& plan) { return plan.n_split > 1 || plan.n_split
 
 template <int D>
 hipError_t launch_d(const Params& prm, const AttnPlan& plan, hipStream_t stream) {
-  const int wgs = (plan.n_cg_full * plan.n_split + plan.n_split_tail) * prm.batch * prm.hkv;
+  const int n_groups = plan.n_cg_full + (plan.n_split_tail > 0 ? 1 : 0);
+  const int max_split = plan.n_split > plan.n_split_tail ? plan.n_split : plan.n_split_tail;
+  const int wgs = n_groups * max_split * prm.batch * prm.hkv;
   constexpr size_t smem = Geo<D>::kSmem;
   if (wgs <= 0) return hipSuccess;
   if (plan_splits(plan)) {
