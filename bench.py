@@ -15,7 +15,10 @@ last-level cache.  All inputs are resident in device memory before timing.
 Prints ONE JSON line.  The step rate comes from replaying one HIP graph per
 input set (every stage of a step in one graph).  Per-stage device times come
 from a second timed region: one graph per stage holding that stage for every
-input set, replayed between HIP events recorded on the launch stream.
+input set, replayed between HIP events recorded on the launch stream.  A third
+region times the same steps with plain launches (no graph).  Side legs time
+the compaction of a 36-layer cache, the tree RoPE/scatter step, packed drafter
+blocks, the ragged serving-batch verify pass and the large logit streams.
 """
 from __future__ import annotations
 
@@ -46,6 +49,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--graph-sets", type=int, default=20,
+                    help="consecutive steps (one per input set) captured in one HIP graph")
     ap.add_argument("--eager", action="store_true",
                     help="launch every stage from Python instead of replaying one HIP graph "
                          "per input set")
@@ -221,6 +226,38 @@ def packed_blocks_leg(torch, ddt, steps, cfg, dev):
             "frac": round(nb_bytes / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def accept_layers_leg(torch, ddt, synth, steps, cases, cfg, dev, n_layers=36):
+    """Acceptance walk + KV compaction over a 36-layer cache (the target
+    model's depth; the step itself compacts one layer) on each input set's own
+    tree, 20 calls per graph, one workgroup per layer.  The target accepts the
+    tree's deepest path (the most rows a tree can move), not the sampled path
+    of the step."""
+    P, N, L = cfg.prefix[0], cfg.B + 1, cfg.L
+    kc = torch.zeros(n_layers, P + N, cfg.hkv, cfg.D, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    base = torch.zeros(1, dtype=torch.int64, device=dev)
+    calls, outs = [], []
+    for s, c in zip(steps, cases):
+        tok = s.tree["token"].cpu().numpy()[0]
+        par = s.tree["parent"].cpu().numpy()[0]
+        dep = s.tree["depth"].cpu().numpy()[0]
+        n = int(s.tree["n_nodes"].item())
+        deepest = int(np.argmax(dep[:n]))
+        tgt = torch.from_numpy(synth.force_path_target(
+            tok, par, dep, n, deepest, c.off_path[0], cfg.vocab)[None]).to(dev)
+        out = {k: torch.empty_like(v) for k, v in s.acc.items()}
+        outs.append(out)
+        calls.append(lambda s=s, out=out, tgt=tgt: ddt.accept_compact(
+            s.tree["token"], s.tree["parent"], s.tree["n_nodes"], tgt, L, kc, vc, base,
+            s.prefix, out=out))
+    t = time_graph(torch, calls, 50)
+    acc = float(np.mean([int(o["accept_len"].item()) for o in outs]))
+    nb = n_layers * acc * cfg.hkv * cfg.D * 2 * 2 * 2   # K and V rows, read + written
+    return {"layers": n_layers, "mean_accept_len": round(acc, 3), "algorithmic_bytes": nb,
+            "bound": "latency", "us": round(t * 1e6, 3),
+            "achieved_gbs": round(nb / t / 1e9, 1)}
+
+
 def serving_verify_leg(args, torch, ddt, synth, dev):
     """Verify attention of the ragged serving batch: 32 requests, 65 tree rows
     each, prefixes U{512..8192}, 32/4/128.  The trees come from this library's
@@ -381,6 +418,7 @@ def main():
     names = ["drafter_attn", "topk", "tree", "verify_attn", "accept"]
 
     stream = torch.cuda.current_stream()
+    G = 1
     if args.eager:
         log(args, f"warmup {args.warmup}")
         for i in range(args.warmup):
@@ -417,15 +455,22 @@ def main():
                     f()
             return g
 
-        graphs = [capture(c) for c in calls]
+        # G consecutive steps (input sets i..i+G-1) per graph; single-step
+        # graphs cover a remainder, so exactly --steps steps run
+        G = max(1, min(args.graph_sets, len(calls)))
+        multi = [capture([f for c in calls[i:i + G] for f in c])
+                 for i in range(0, len(calls) - G + 1, G)]
+        single = [capture(c) for c in calls]
         log(args, f"warmup {args.warmup}")
         for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
+            single[i % len(single)].replay()
         torch.cuda.synchronize()
-        log(args, f"timing {args.steps} graph steps")
+        log(args, f"timing {args.steps} graph steps, {G} per graph")
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % len(graphs)].replay()
+        for i in range(args.steps // G):
+            multi[i % len(multi)].replay()
+        for i in range(args.steps % G):
+            single[i % len(single)].replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         # region B: per-stage device time.  One graph per stage holds that
@@ -449,6 +494,20 @@ def main():
             ev.append((a, b))
         torch.cuda.synchronize()
         log(args, f"timed {reps} replays of {len(calls)} launches per stage")
+        # region C: the same step with plain launches (one ctypes call per
+        # stage from Python, no graph), for comparison with region A
+        n_eager = min(args.steps, 500)
+        for i in range(5):
+            for f in calls[i % len(calls)]:
+                f()
+        torch.cuda.synchronize()
+        te0 = time.perf_counter()
+        for i in range(n_eager):
+            for f in calls[i % len(calls)]:
+                f()
+        torch.cuda.synchronize()
+        eager_ms = (time.perf_counter() - te0) * 1e3 / n_eager
+        log(args, f"timed {n_eager} plain-launch steps")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     stage_ms = np.zeros(len(names))
     if args.eager:
@@ -498,7 +557,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "launch": "eager" if args.eager else "hip_graph_per_step",
+        "launch": "eager" if args.eager else f"hip_graph ({G} steps per graph)",
         "config": {
             "workload": "ddtree_step_c3: L=16 V=151936 K=32 B=256 k_tree=32; drafter 16q over "
                         "2048+16 rows; verify 257q over 2048+257 rows; hq=32 hkv=8 D=128; "
@@ -529,6 +588,10 @@ def main():
         },
     }
 
+    if not args.eager:
+        result["plain_launches"] = {"steps": n_eager, "ms_per_step": round(eager_ms, 5),
+                                    "steps_per_s": round(1e3 / eager_ms, 2)}
+    result["accept_36_layers"] = accept_layers_leg(torch, ddt, synth, steps, cases, cfg, dev)
     result["tree_rope_kv"] = tree_rope_leg(torch, ddt, steps, cfg, dev)
     result["packed_blocks_attn"] = packed_blocks_leg(torch, ddt, steps, cfg, dev)
     if not args.no_streams:
