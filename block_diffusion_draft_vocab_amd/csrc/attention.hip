@@ -110,9 +110,14 @@ struct Params {
 
 // Tiles [t0, t1) of split s out of n_split over nt tiles (balanced; 32-bit
 // products: n_split <= 2^15 and nt < 2^16 under the plan's limits).
+// Tiles [t0, t1) of split s: nt / n_split each, the remainder one apiece to
+// the first splits.  Those are dispatched first, and the last split, which
+// holds the own rows (and their visibility setup), stays among the short ones.
 __device__ __forceinline__ void split_range(int s, int n_split, int nt, int& t0, int& t1) {
-  t0 = (int)((uint32_t)(s * nt) / (uint32_t)n_split);
-  t1 = (int)((uint32_t)((s + 1) * nt) / (uint32_t)n_split);
+  const int q = nt / n_split;
+  const int rem = nt - q * n_split;
+  t0 = s * q + (s < rem ? s : rem);
+  t1 = t0 + q + (s < rem ? 1 : 0);
 }
 // Key splits request r actually uses: the plan's count scaled by the
 // request's share of the longest key range, so that a short request in a
@@ -364,8 +369,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   // windows of the range's own-row tiles are computed here once (their mask
   // words loaded together: one memory latency) and kept in LDS, so the tile
   // loop issues no memory operation besides the tile copies.
+  // Without a mask or packed blocks every own key is visible to every
+  // column: no tile is skipped and the loop derives its windows from P and nq.
   const int nt_range = t_end - t_begin;
-  const bool listed = t_end * kKT > P;
+  const bool listed = (has_mask || p.block_len > 0) && t_end * kKT > P;
   int ntl = nt_range;
   if (listed) {
     for (int i = tid; i < nt_range; i += kThreads) own_need[i] = 0u;
@@ -496,7 +503,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
         xv[16 + v] = sb[v];
       }
     } else {
-      const uint64_t win = win_lds[ti - t_begin][wid * kColsPerWave + n] >> (4 * h2);
+      const uint64_t win =
+          (listed ? win_lds[ti - t_begin][wid * kColsPerWave + n]
+                  : (valid ? visible64(key0, P, 0, nq, false, 0ull, 0ull) : 0ull)) >>
+          (4 * h2);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kk = (v >> 2) * 8 + (v & 3);
