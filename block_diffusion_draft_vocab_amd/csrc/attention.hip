@@ -253,6 +253,15 @@ __device__ __forceinline__ void wait_vm() {
 template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   using G = Geo<D>;
+  // Every parameter is read here, before the first branch.  Left alone, the
+  // compiler sinks each scalar load to its first use behind the early exits,
+  // and a workgroup pays one scalar round trip per use before its first tile
+  // copy.  (Input operands only: the pointers keep their address space.)
+  asm volatile("" ::"s"(p.q), "s"(p.k), "s"(p.v), "s"(p.kv_base), "s"(p.prefix_len), "s"(p.n_q));
+  asm volatile("" ::"s"(p.mask), "s"(p.out), "s"(p.lse), "s"(p.part_o), "s"(p.part_ml));
+  asm volatile("" ::"s"(p.batch), "s"(p.hq), "s"(p.hkv), "s"(p.n_q_max), "s"(p.mask_words),
+               "s"(p.n_cg_full), "s"(p.n_split), "s"(p.n_split_tail), "s"(p.max_tiles),
+               "s"(p.block_len), "s"(p.scale_log2));
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
   __shared__ int tile_list[kMaxTilesPerSplit];
   __shared__ int n_tiles_s;
@@ -278,8 +287,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int s = x / n_groups;
   int n_split = cg < p.n_cg_full ? p.n_split : p.n_split_tail;
 
+  // the request's sizes and cache base: three loads, one round trip
   const int P = p.prefix_len[r];
-  const int nq = min(p.n_q[r], p.n_q_max);
+  const int nq_req = p.n_q[r];
+  const int64_t base = p.kv_base[r];
+  asm volatile("" ::"s"(P), "s"(nq_req), "s"(base));
+  const int nq = min(nq_req, p.n_q_max);
   const int T = P + nq;
   const int g = p.hq / p.hkv;
   const int ncols = nq * g;
@@ -295,7 +308,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   // prefix_len + n_q is within the max_kv_len the plan was made for; the
   // clamp only keeps a violated bound from indexing past the tile list
   if (t_end - t_begin > kMaxTilesPerSplit) t_end = t_begin + kMaxTilesPerSplit;
-  const int64_t base = p.kv_base[r];
   const bool wave_active = col0 + wid * kColsPerWave < ncols;
   const bool has_mask = p.mask != nullptr;
 
