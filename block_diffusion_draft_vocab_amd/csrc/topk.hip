@@ -175,28 +175,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     part_ms[(int64_t)row * n_chunks + chunk] = make_float2(M, S);
   }
   // gather the keys >= T (T == 0 means every valid key, i.e. every finite
-  // x): the wave's count from per-slot ballots, one LDS atomic per wave,
-  // then one pass over the element slots that any lane of the wave selected
+  // x).  Only lanes whose own maximum reaches T hold such keys: they count
+  // them, a wave prefix sum of the counts and one LDS atomic per wave give
+  // each lane its first slot, and the lanes write their keys in element
+  // order.  Waves without such a lane skip both passes.
   {
     const float tf = T == 0u ? -3.402823466e38f : f32_unorder(T);
-    int total = 0;
+    const bool holder = tm >= tf;
+    int mine = 0;
+    if (holder) {
 #pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i) total += __popcll(__ballot(x[i] >= tf));
+      for (int i = 0; i < kTopkPerThread; ++i) mine += x[i] >= tf ? 1 : 0;
+    }
+    const int incl = wave_inclusive_scan(mine);
+    const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
     int base = 0;
     if (lane == 0 && total > 0) base = atomicAdd(&sm.cand_n, total);
     base = __builtin_amdgcn_readfirstlane(base);
+    if (holder) {
+      int pos = base + incl - mine;
 #pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i) {
-      const bool take = x[i] >= tf;
-      const uint64_t bal = __ballot(take);
-      if (bal != 0) {
-        if (take) {
-          const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      for (int i = 0; i < kTopkPerThread; ++i) {
+        if (x[i] >= tf) {
           const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
           if (pos < kCandCap) sm.cand[pos] = make_key(x[i], idx);
+          ++pos;
         }
-        base += __popcll(bal);
       }
     }
   }
