@@ -148,15 +148,16 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       if (is) slot_tab[q] = __popcll(bal & lanemask_lt());
     }
     __syncthreads();
-    int n = 0;
-    for (int c = 0; c < nchunk; ++c) n += wcnt[c];
+    // inclusive prefix of the chunk counts across the lanes of every wave
+    // (nchunk <= 32); q / 64 is uniform across a wave in the loop below
+    const int cinc = wave_inclusive_scan(lane < nchunk ? wcnt[lane] : 0);
+    const int n = __builtin_amdgcn_readlane(cinc, kWave - 1);
     if (n == 0) break;
     for (int q = tid; q < g; q += nt) {
+      const int c = q / kWave;
+      const int pre = c > 0 ? __builtin_amdgcn_readlane(cinc, c - 1) : 0;
       const uint64_t kq = gb[q];
-      if (key_depth(kq) != d - 1) continue;
-      int pre = 0;
-      for (int c = 0; c < q / kWave; ++c) pre += wcnt[c];
-      pscore[pre + slot_tab[q]] = key_score(kq);
+      if (key_depth(kq) == d - 1) pscore[pre + slot_tab[q]] = key_score(kq);
     }
     __syncthreads();
     // run length of parent j: children (j, c) with key above theta and
@@ -188,12 +189,9 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     const int inc = wave_inclusive_scan(mine);
     if (lane == kWave - 1) misc[8 + wid] = inc;
     __syncthreads();
-    int wpre = 0, nc = 0;
-    for (int w = 0; w < nwaves; ++w) {
-      const int t = misc[8 + w];
-      wpre += w < wid ? t : 0;
-      nc += t;
-    }
+    const int winc = wave_inclusive_scan(lane < nwaves ? misc[8 + lane] : 0);
+    const int wpre = wid > 0 ? __builtin_amdgcn_readlane(winc, wid - 1) : 0;
+    const int nc = __builtin_amdgcn_readlane(winc, kWave - 1);
     {
       int o = wpre + inc - mine;
 #pragma unroll
