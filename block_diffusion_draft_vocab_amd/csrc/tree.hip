@@ -135,8 +135,20 @@ __global__ __launch_bounds__(1024) void tree_kernel(
   __syncthreads();
   uint64_t theta = (g == B && B > 0) ? gb[B - 1] : 0ull;
   const int nwaves = nt / kWave;
+  // score of the best depth-(d-1) node: the rank-0 child of the previous
+  // level's first parent (depth 1: rank 0 of row 0)
+  float best_prev = y[0];
 
   for (int d = 2; d <= L && g > 0; ++d) {
+    // The level's best possible child is the rank-0 child of its first
+    // parent (the best depth-(d-1) node, which is in G: it beat theta when
+    // it was made, so the top-B cut kept it); every other child has a lower
+    // or equal score and a later tie-break.  When that one does not beat
+    // theta the level adds nothing, and neither does any deeper one.
+    const float* yd = y + (d - 1) * k_tree;
+    const float best_child = best_prev + yd[0];
+    if (g == B && !(tkey(best_child, d, 0, 0) > theta)) break;
+    best_prev = best_child;
     // parents: the depth d-1 members of G, numbered in G order (a ballot
     // per 64-position chunk, then the chunk counts summed directly)
     const int nchunk = (g + kWave - 1) / kWave;
@@ -164,7 +176,6 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     // (j+1)(c+1) <= B; keys fall with c, so a binary search finds it.
     // Thread t owns parents [t*per, t*per + per).
     // (n <= B < 2 * nt: the launch gives max(cand_cap, 1024) threads or more)
-    const float* yd = y + (d - 1) * k_tree;
     const int per = (n + nt - 1) / nt;
     int lens[2] = {0, 0};
     int mine = 0;
