@@ -144,7 +144,8 @@ def _random_tree_mask(rng, n, n_max):
 
 @pytest.mark.parametrize("D,hq,hkv,prefix,n_q,nq_max", [
     (128, 8, 8, [33], [5], 5), (64, 16, 2, [0, 70], [9, 40], 40), (32, 4, 1, [1, 95, 31], [1, 3, 64], 64),
-    (128, 32, 4, [517, 1000], [65, 12], 65), (64, 8, 2, [64], [130], 130), (32, 2, 2, [10], [70], 70)])
+    (128, 32, 4, [517, 1000], [65, 12], 65), (64, 8, 2, [64], [130], 130), (32, 2, 2, [10], [70], 70),
+    (64, 8, 2, [50, 70], [0, 9], 9)])     # an empty request beside a short one
 @pytest.mark.parametrize("masked", [True, False], ids=["verify", "drafter"])
 def test_edge_shapes(gpu, D, hq, hkv, prefix, n_q, nq_max, masked):
     seed = D + hq * 7 + sum(prefix) + sum(n_q)
