@@ -67,6 +67,7 @@ struct PartialSmem {
   alignas(16) uint64_t cand[kCandCap];
 };
 
+template <int PER>
 __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     const float* __restrict__ logits, int64_t ld, int vocab, int k, float inv_t, int chunk_len,
     int n_chunks, uint64_t* __restrict__ part_key, float2* __restrict__ part_ms) {
@@ -87,16 +88,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
   // element i of this thread is index c0 + ((i/4) * 256 + tid) * 4 + i%4.
   // Every load is issued unconditionally (out-of-range ones from c0), so
   // all of them are in flight together; the values are masked afterwards.
-  float x[kTopkPerThread];
+  float x[PER];
   if (vec) {
-    float4 v[kTopkPerThread / 4];
+    float4 v[PER / 4];
 #pragma unroll
-    for (int q = 0; q < kTopkPerThread / 4; ++q) {
+    for (int q = 0; q < PER / 4; ++q) {
       const int b = c0 + (q * kTopkThreads + tid) * 4;
       v[q] = load_f4_stream(rp + (b + 3 < c1 ? b : c0));
     }
 #pragma unroll
-    for (int q = 0; q < kTopkPerThread / 4; ++q) {
+    for (int q = 0; q < PER / 4; ++q) {
       const int b = c0 + (q * kTopkThreads + tid) * 4;
       const bool full = b + 3 < c1;
       x[4 * q + 0] = full ? v[q].x * inv_t : -INFINITY;
@@ -109,21 +110,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
       }
     }
   } else {
-    float y[kTopkPerThread];
+    float y[PER];
 #pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
       y[i] = rp[idx < c1 ? idx : c0];
     }
 #pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i) {
+    for (int i = 0; i < PER; ++i) {
       const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
       x[i] = idx < c1 ? y[i] * inv_t : -INFINITY;
     }
   }
   float tm = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kTopkPerThread; ++i) tm = fmaxf(tm, x[i]);
+  for (int i = 0; i < PER; ++i) tm = fmaxf(tm, x[i]);
   const float wm = wave_max_f(tm);
   sm.lanemax[tid] = f32_order(tm);
   if (lane == 0) sm.wmax[wid] = wm;
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
   if (M != -INFINITY) {
     const float mb = M * kLog2e;
 #pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i) s += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mb));
+    for (int i = 0; i < PER; ++i) s += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mb));
   }
   const float ws = wave_sum_f(s);
   if (lane == 0) sm.wsum[wid] = ws;
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     int mine = 0;
     if (holder) {
 #pragma unroll
-      for (int i = 0; i < kTopkPerThread; ++i) mine += x[i] >= tf ? 1 : 0;
+      for (int i = 0; i < PER; ++i) mine += x[i] >= tf ? 1 : 0;
     }
     const int incl = wave_inclusive_scan(mine);
     const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     if (holder) {
       int pos = base + incl - mine;
 #pragma unroll
-      for (int i = 0; i < kTopkPerThread; ++i) {
+      for (int i = 0; i < PER; ++i) {
         if (x[i] >= tf) {
           const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
           if (pos < kCandCap) sm.cand[pos] = make_key(x[i], idx);
@@ -218,9 +219,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     return;
   }
   // exact fallback for massive ties: k rounds of a block-wide arg-max
-  uint64_t key[kTopkPerThread];
+  uint64_t key[PER];
 #pragma unroll
-  for (int i = 0; i < kTopkPerThread; ++i) {
+  for (int i = 0; i < PER; ++i) {
     const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
     key[i] = idx < c1 ? make_key(x[i], idx) : 0ull;
   }
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
   for (int j = 0; j < k; ++j) {
     uint64_t b = 0;
 #pragma unroll
-    for (int i = 0; i < kTopkPerThread; ++i)
+    for (int i = 0; i < PER; ++i)
       if (key[i] < prev && key[i] > b) b = key[i];
     __syncthreads();
     red[tid] = b;
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
   __shared__ alignas(16) uint64_t take_all[kWaves][kWaveCandCap];
   const int wid = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int row = blockIdx.x * kWaves + wid;
+  const int row = blockIdx.x * (int)(blockDim.x / kWave) + wid;
   if (row >= n_rows) return;
   const int n = n_chunks * k;
   const uint64_t* lists = part_key + (int64_t)row * n;
@@ -572,9 +573,16 @@ hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, i
   uint64_t* part_key = static_cast<uint64_t*>(ws);
   float2* part_ms = reinterpret_cast<float2*>(
       static_cast<char*>(ws) + align256((size_t)n_rows * p.n_chunks * k * sizeof(uint64_t)));
-  hipLaunchKernelGGL(topk_partial_kernel, dim3(p.n_chunks, n_rows), dim3(kTopkThreads), 0,
-                     stream, logits, ld, vocab, k, inv_t, p.chunk_len, p.n_chunks, part_key,
-                     part_ms);
+  // 20 floats per thread when the chunk fits them (fewer loads and
+  // registers for the short chunks of a few rows), else 32
+  if (p.chunk_len <= kTopkThreads * 20)
+    hipLaunchKernelGGL(topk_partial_kernel<20>, dim3(p.n_chunks, n_rows), dim3(kTopkThreads), 0,
+                       stream, logits, ld, vocab, k, inv_t, p.chunk_len, p.n_chunks, part_key,
+                       part_ms);
+  else
+    hipLaunchKernelGGL(topk_partial_kernel<kTopkPerThread>, dim3(p.n_chunks, n_rows),
+                       dim3(kTopkThreads), 0, stream, logits, ld, vocab, k, inv_t, p.chunk_len,
+                       p.n_chunks, part_key, part_ms);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_merge(part_key, part_ms, n_rows, p.n_chunks, k, ids, logp, lse, stream);
@@ -586,9 +594,12 @@ hipError_t launch_topk_merge(const uint64_t* part_key, const float2* part_ms, in
   const int n = n_chunks * k;
   const int ns = n_chunks * ((k + n_chunks - 1) / n_chunks);
   if (n <= 64 * 32 && ns <= kWave && n_chunks <= 2 * kWave) {
-    const dim3 grid((n_rows + kWaves - 1) / kWaves);
+    // one wave per workgroup for a few rows (each row's merge on its own
+    // CU), four for many
+    const int wpb = n_rows <= 64 ? 1 : kWaves;
+    const dim3 grid((n_rows + wpb - 1) / wpb);
 #define DDT_MERGE_WAVE(RR)                                                                    \
-  hipLaunchKernelGGL(topk_merge_wave_kernel<RR>, grid, dim3(kTopkThreads), 0, stream, part_key, \
+  hipLaunchKernelGGL(topk_merge_wave_kernel<RR>, grid, dim3(wpb * kWave), 0, stream, part_key, \
                      part_ms, n_rows, n_chunks, k, ids, logp, lse)
     if (n <= 64 * 4) DDT_MERGE_WAVE(4);
     else if (n <= 64 * 8) DDT_MERGE_WAVE(8);
