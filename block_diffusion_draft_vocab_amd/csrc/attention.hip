@@ -654,9 +654,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
   constexpr int kTPR = D / 8;
-  constexpr int kRPB = 256 / kTPR;
   constexpr int kBatch = 16;
-  const int gid = blockIdx.x * kRPB + threadIdx.x / kTPR;
+  const int gid = blockIdx.x * (int)(blockDim.x / kTPR) + threadIdx.x / kTPR;
   const int lane = threadIdx.x % kTPR;
   if (gid >= p.batch * p.n_q_max * p.hq) return;
   const int head = gid % p.hq;
@@ -731,9 +730,12 @@ hipError_t launch_d(const Params& prm, const AttnPlan& plan, hipStream_t stream)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<D, true>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     hipLaunchKernelGGL((attn_kernel<D, true>), dim3(wgs), dim3(kThreads), smem, stream, prm);
+    // 256-thread workgroups, or 64 when that leaves most CUs idle (a
+    // drafter block's few rows: every CU then holds some of the loads)
     const int rows = prm.batch * prm.n_q_max * prm.hq;
-    const int rpb = 256 / (D / 8);
-    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(256), 0,
+    const int threads = (long)rows * (D / 8) < 256L * kCUs ? 64 : 256;
+    const int rpb = threads / (D / 8);
+    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(threads), 0,
                        stream, prm);
   } else {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<D, false>),
