@@ -534,7 +534,10 @@ def main():
     logit_gbs = logit_bytes / t_logit / 1e9
     verify_tflops = verify_flops / t_verify / 1e12
 
-    traffic = None
+    # HBM bytes and MFMA counters of the verify launch, from the rocprofv3
+    # counter passes summarised under profiles/ (only while attention.hip
+    # is the source they were taken from)
+    traffic = issued_mfma = mfma_busy = None
     tfile = os.path.join(ROOT, "profiles", "verify_attn_traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
@@ -543,6 +546,8 @@ def main():
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
         if tr.get("source_sha256") == sha:
             traffic = tr.get("hbm_bytes_per_launch")
+            issued_mfma = tr.get("issued_mfma_bf16_flops_per_launch")
+            mfma_busy = tr.get("mfma_busy_pct_main_kernel")
 
     result = {
         "metric": METRIC,
@@ -573,6 +578,8 @@ def main():
             "frac": round(verify_tflops / BF16_PEAK_TFLOPS, 5),
             "traffic": traffic,
             "algorithmic_flops_per_launch": verify_flops,
+            "issued_mfma_flops_per_launch": issued_mfma,
+            "mfma_busy_pct_main_kernel": mfma_busy,
         },
         "stages_us": {n: round(float(m) * 1e3, 3) for n, m in zip(names, stage_ms)},
         "logit_pass": {
