@@ -126,6 +126,9 @@ hipError_t launch_accept(const int32_t* token, const int32_t* parent, const int3
                          int32_t* new_len, hipStream_t stream) {
   const size_t smem = (size_t)(n_max + L + 1 + 2) * sizeof(int);
   const int layers = n_layers > 0 ? n_layers : 1;
+  if (smem > 64 * 1024)  // slot arrays past about 16,000 entries
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(accept_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   hipLaunchKernelGGL(accept_kernel, dim3(batch, layers), dim3(kAcceptThreads), smem, stream,
                      token, parent, n_nodes, n_max, target, L,
                      static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), kv_base,

@@ -142,3 +142,37 @@ def test_no_layers(gpu):
     assert out["accept_len"].item() == 2 and out["bonus"].item() == 9
     assert out["new_len"].item() == 103
     assert out["accepted"].cpu().tolist() == [[0, 1, 2, -1, -1]]
+
+
+def test_wide_slot_arrays(gpu):
+    """n_max = 20000 (the walk's slot table is 80 KB of on-chip memory): a
+    five-node tree in wide arrays walks and compacts as the oracle does."""
+    n_max, L = 20000, 4
+    tok = np.full((1, n_max), -1, np.int32)
+    par = np.full((1, n_max), -1, np.int32)
+    tgt = np.full((1, n_max), 7, np.int32)
+    tok[0, :5] = [5, 1, 3, 8, 2]
+    par[0, :5] = [-1, 0, 0, 1, 2]
+    tgt[0, :5] = [3, 4, 2, 4, 9]          # root -> slot 2 -> slot 4, bonus 9
+    rows, hkv, D, P = 64, 2, 16, 40
+    rng = np.random.default_rng(5)
+    kbits = rng.integers(0, 2 ** 15, size=(1, rows, hkv, D), dtype=np.int64).astype(np.uint16)
+    vbits = rng.integers(0, 2 ** 15, size=(1, rows, hkv, D), dtype=np.int64).astype(np.uint16)
+    kc = torch.from_numpy(kbits.view(np.int16)).to(gpu).view(torch.bfloat16)
+    vc = torch.from_numpy(vbits.view(np.int16)).to(gpu).view(torch.bfloat16)
+    base = np.zeros(1, np.int64)
+    prefix = np.array([P], np.int32)
+    nn = np.array([5], np.int32)
+    out = ddt.accept_compact(torch.from_numpy(tok).to(gpu), torch.from_numpy(par).to(gpu),
+                             torch.from_numpy(nn).to(gpu), torch.from_numpy(tgt).to(gpu), L,
+                             kc, vc, torch.from_numpy(base).to(gpu),
+                             torch.from_numpy(prefix).to(gpu))
+    torch.cuda.synchronize()
+    oacc, opath, obonus, onew, okc, ovc = oracle_accept(tok, par, nn, tgt, L, kbits, vbits, base,
+                                                        prefix)
+    assert out["accept_len"].item() == int(oacc[0]) == 2
+    assert out["bonus"].item() == int(obonus[0]) == 9
+    assert out["new_len"].item() == int(onew[0]) == P + 3
+    assert out["accepted"].cpu().tolist() == [[0, 2, 4, -1, -1]]
+    assert np.array_equal(host_bf16_bits(kc), okc)
+    assert np.array_equal(host_bf16_bits(vc), ovc)
