@@ -253,6 +253,7 @@ DDT_EXPORT int ddt_accept_compact(const int32_t* node_token, const int32_t* node
       return DDT_EINVAL;
   }
   if ((size_t)(n_max + L + 3) * sizeof(int) > kMaxLds) return DDT_EUNSUPPORTED;
+  if (n_layers > 65535) return DDT_EUNSUPPORTED;  // layers are the grid's y dimension
   return launch_status(ddt::launch_accept(node_token, node_parent, n_nodes, n_max,
                                           target_argmax, batch, L, k_cache, v_cache, kv_base,
                                           prefix_len, n_layers, layer_stride_elems, hkv,

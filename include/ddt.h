@@ -339,7 +339,8 @@ int ddt_packed_block_attention(const ddt_attn_desc* desc, int block_len, const v
  * Rows >= new_len of the request are unspecified afterwards.
  * Errors: EINVAL if batch < 1, n_max < 1, L < 1, n_layers < 0, hkv < 1,
  *         head_dim < 1, hkv*head_dim not a multiple of 8, or a required
- *         pointer is NULL.
+ *         pointer is NULL; EUNSUPPORTED if n_layers > 65535 or the slot
+ *         table (n_max + L + 3 words) exceeds 160 KiB of on-chip memory.
  * Preconditions (device): a tree as ddt_build_tree writes it (parents
  *   precede children, sibling tokens distinct, depth <= L).
  * ---------------------------------------------------------------------- */

@@ -212,3 +212,5 @@ def test_accept_validation(lib):
     assert _accept(lib, kc=None) == E.DDT_EINVAL
     assert _accept(lib, kc=ctypes.c_void_p(264)) == E.DDT_EINVAL
     assert _accept(lib, stride=12) == E.DDT_EINVAL
+    assert _accept(lib, n_layers=65536) == E.DDT_EUNSUPPORTED
+    assert _accept(lib, n_max=41000) == E.DDT_EUNSUPPORTED     # slot table > 160 KiB
