@@ -549,6 +549,16 @@ def main():
             issued_mfma = tr.get("issued_mfma_bf16_flops_per_launch")
             mfma_busy = tr.get("mfma_busy_pct_main_kernel")
 
+    # HBM bytes per launch of the logit pass and the drafter pass, likewise
+    stage_traffic = {}
+    sfile = os.path.join(ROOT, "profiles", "step_stage_traffic.json")
+    if os.path.exists(sfile):
+        with open(sfile) as f:
+            for name, tr in json.load(f).items():
+                src = os.path.join(ROOT, tr["source"])
+                if hashlib.sha256(open(src, "rb").read()).hexdigest() == tr.get("source_sha256"):
+                    stage_traffic[name] = tr.get("hbm_bytes_per_launch")
+
     result = {
         "metric": METRIC,
         "value": round(steps_per_s, 2),
@@ -585,13 +595,13 @@ def main():
         "logit_pass": {
             "bound": "hbm", "achieved": round(logit_gbs, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(logit_gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": logit_bytes,
+            "algorithmic_bytes": logit_bytes, "traffic": stage_traffic.get("logit_pass"),
         },
         "drafter_attn": {
             "bound": "hbm", "achieved": round(drafter_bytes / t_draft / 1e9, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(drafter_bytes / t_draft / 1e9 / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": drafter_bytes,
+            "algorithmic_bytes": drafter_bytes, "traffic": stage_traffic.get("drafter_attn"),
         },
     }
 
