@@ -78,8 +78,10 @@ def test_verify_full_size(gpu, cfg):
     _compare(out, lse, oout, olse, case.prefix_len, n_q)
 
 
-def test_verify_large_budget(gpu):
-    cfg = synth.CONFIGS[4]
+@pytest.mark.parametrize("cfg", [synth.CONFIGS[4], synth.FLAT4], ids=["c4", "c4flat"])
+def test_verify_large_budget(gpu, cfg):
+    """Budget 1024 over a 4096-row prefix, peaked and flat draft distributions
+    (the flat one spreads the tree: more depth-1 branches, sparser masks)."""
     case = synth.make_case(cfg, with_drafter=False)
     t = _tree_masks(cfg, case)
     N = cfg.B + 1
