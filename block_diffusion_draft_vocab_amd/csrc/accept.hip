@@ -12,8 +12,10 @@
 //             write is race-free)
 //   the path follows next[] from the root (at most L steps).
 // Compaction moves rows P + path[j] -> P + j.  A destination row can be the
-// source of a later path entry, so each pass loads every source segment of
-// a column range into registers, waits at a barrier, and only then stores.
+// source of an earlier path entry (path[j'] = j with j' < j), so each round
+// loads every source segment of its entries and columns into registers,
+// waits at a barrier, and only then stores; rounds take the entries in
+// increasing order.
 #include "common.h"
 #include "launch.h"
 
@@ -82,37 +84,46 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
   cols = cols < 1 ? 1 : cols;
   for (int c0 = 0; c0 < nch; c0 += cols) {
     const int cw = min(cols, nch - c0);
-    const int per_tensor = len * cw;
-    const int items = 2 * per_tensor;
-    u32x4 regs[kRegs];
+    // Path entries per round: all of them unless the path is longer than one
+    // round of registers holds.  Rounds go in increasing entry order: entry
+    // j's destination row P + j can only be the source of an earlier entry
+    // (path slots increase along the path and path[j] >= j), which an
+    // earlier round (or the gather before this round's barrier) has read.
+    const int jb = max(1, per_round / (2 * cw));
+    for (int j0 = 1; j0 <= len; j0 += jb) {
+      const int nj = min(jb, len - j0 + 1);
+      const int per_tensor = nj * cw;
+      const int items = 2 * per_tensor;  // <= per_round
+      u32x4 regs[kRegs];
 #pragma unroll
-    for (int i = 0; i < kRegs; ++i) {
-      const int it = tid + i * kAcceptThreads;
-      if (it < items) {
-        const int tsel = it / per_tensor;
-        const int rem = it - tsel * per_tensor;
-        const int j = rem / cw + 1;
-        const int c = c0 + (rem - (j - 1) * cw);
-        const uint16_t* base = (tsel == 0 ? k_cache : v_cache) + layer * layer_stride;
-        regs[i] = *reinterpret_cast<const u32x4*>(base + (row0 + path[j]) * row_elems + c * 8);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kRegs; ++i) {
-      const int it = tid + i * kAcceptThreads;
-      if (it < items) {
-        const int tsel = it / per_tensor;
-        const int rem = it - tsel * per_tensor;
-        const int j = rem / cw + 1;
-        const int c = c0 + (rem - (j - 1) * cw);
-        if (path[j] != j) {
-          uint16_t* base = (tsel == 0 ? k_cache : v_cache) + layer * layer_stride;
-          *reinterpret_cast<u32x4*>(base + (row0 + j) * row_elems + c * 8) = regs[i];
+      for (int i = 0; i < kRegs; ++i) {
+        const int it = tid + i * kAcceptThreads;
+        if (it < items) {
+          const int tsel = it / per_tensor;
+          const int rem = it - tsel * per_tensor;
+          const int j = j0 + rem / cw;
+          const int c = c0 + rem % cw;
+          const uint16_t* base = (tsel == 0 ? k_cache : v_cache) + layer * layer_stride;
+          regs[i] = *reinterpret_cast<const u32x4*>(base + (row0 + path[j]) * row_elems + c * 8);
         }
       }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kRegs; ++i) {
+        const int it = tid + i * kAcceptThreads;
+        if (it < items) {
+          const int tsel = it / per_tensor;
+          const int rem = it - tsel * per_tensor;
+          const int j = j0 + rem / cw;
+          const int c = c0 + rem % cw;
+          if (path[j] != j) {
+            uint16_t* base = (tsel == 0 ? k_cache : v_cache) + layer * layer_stride;
+            *reinterpret_cast<u32x4*>(base + (row0 + j) * row_elems + c * 8) = regs[i];
+          }
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 

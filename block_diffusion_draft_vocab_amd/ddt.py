@@ -8,6 +8,7 @@ loading fails loudly otherwise -- there is no CPU fallback.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -89,9 +90,22 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream=None):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _on_stream(fn):
+    """Run an entry point with ``stream=`` as torch's current stream, so the
+    outputs and the workspace it allocates belong to the stream its kernels
+    run on (the caching allocator then cannot hand their blocks to other
+    work before those kernels finish)."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kw)
+    return wrapper
 
 
 def _need(t: torch.Tensor, dtype, name: str):
@@ -118,9 +132,10 @@ def topk_workspace_size(n_rows: int, vocab: int, k: int) -> int:
     return int(load().ddt_topk_logprobs_workspace_size(n_rows, vocab, k))
 
 
+@_on_stream
 def topk_logprobs(logits: torch.Tensor, k: int, inv_temperature: float = 1.0, *,
                   vocab: Optional[int] = None, ids=None, logp=None, lse=None, workspace=None,
-                  want_lse: bool = True, stream=None):
+                  want_lse: bool = True):
     lib = load()
     if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_cuda:
         raise ValueError("logits must be a device float32 [rows, ld] tensor")
@@ -135,7 +150,7 @@ def topk_logprobs(logits: torch.Tensor, k: int, inv_temperature: float = 1.0, *,
         lse = torch.empty(rows, dtype=torch.float32, device=dev)
     ws, wsb = _workspace(topk_workspace_size(rows, vocab, k), dev, workspace)
     st = lib.ddt_topk_logprobs(_ptr(logits), ld, rows, vocab, k, float(inv_temperature),
-                               _ptr(ids), _ptr(logp), _ptr(lse), _ptr(ws), wsb, _stream(stream))
+                               _ptr(ids), _ptr(logp), _ptr(lse), _ptr(ws), wsb, _stream())
     _check("ddt_topk_logprobs", st)
     return ids, logp, lse
 
@@ -145,9 +160,10 @@ def lmhead_topk_workspace_size(n_rows: int, hidden: int, vocab: int, k: int) -> 
     return int(load().ddt_lmhead_topk_workspace_size(n_rows, hidden, vocab, k))
 
 
+@_on_stream
 def lmhead_topk(hidden_states: torch.Tensor, weight: torch.Tensor, k: int,
                 inv_temperature: float = 1.0, *, ids=None, logp=None, lse=None, workspace=None,
-                want_lse: bool = True, stream=None):
+                want_lse: bool = True):
     """Top-k ids / log-probs of softmax(inv_temperature * hidden_states . weight^T)
     per row, without materialising the logits.  hidden_states bf16 [rows, hidden],
     weight bf16 [vocab, hidden] (the LM head), both contiguous on the device."""
@@ -166,17 +182,17 @@ def lmhead_topk(hidden_states: torch.Tensor, weight: torch.Tensor, k: int,
     ws, wsb = _workspace(lmhead_topk_workspace_size(rows, hidden, vocab, k), dev, workspace)
     st = lib.ddt_lmhead_topk(_ptr(hidden_states), _ptr(weight), rows, hidden, vocab, k,
                              float(inv_temperature), _ptr(ids), _ptr(logp), _ptr(lse), _ptr(ws),
-                             wsb, _stream(stream))
+                             wsb, _stream())
     _check("ddt_lmhead_topk", st)
     return ids, logp, lse
 
 
 # ---------------------------------------------------------------- tree RoPE + KV
+@_on_stream
 def tree_rope_kv(node_depth: torch.Tensor, n_nodes: torch.Tensor, prefix_len: torch.Tensor,
                  kv_base: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
                  v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                 rope_base: float = 1.0e6, *, positions=None, want_positions: bool = True,
-                 stream=None):
+                 rope_base: float = 1.0e6, *, positions=None, want_positions: bool = True):
     """Positions P + depth for the tree slots, rotary embedding of q (in place)
     and of the new k, and the scatter of k / v into the cache rows P + slot.
     Returns positions i32 [batch, n_max] (or None)."""
@@ -199,7 +215,7 @@ def tree_rope_kv(node_depth: torch.Tensor, n_nodes: torch.Tensor, prefix_len: to
     st = lib.ddt_tree_rope_kv(_ptr(node_depth), _ptr(n_nodes), batch, n_max, _ptr(prefix_len),
                               _ptr(kv_base), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
                               _ptr(v_cache), hq, hkv, D, float(rope_base), _ptr(positions),
-                              _stream(stream))
+                              _stream())
     _check("ddt_tree_rope_kv", st)
     return positions
 
@@ -209,8 +225,9 @@ def argmax_workspace_size(n_rows: int, vocab: int) -> int:
     return int(load().ddt_argmax_workspace_size(n_rows, vocab))
 
 
+@_on_stream
 def argmax(logits: torch.Tensor, *, vocab: Optional[int] = None, ids=None, maxv=None,
-           want_max: bool = False, workspace=None, stream=None):
+           want_max: bool = False, workspace=None):
     """Per-row arg-max (smallest id among the maxima) of device float32 logits.
     Returns (ids i32 [rows], max f32 [rows] or None)."""
     lib = load()
@@ -226,15 +243,15 @@ def argmax(logits: torch.Tensor, *, vocab: Optional[int] = None, ids=None, maxv=
         maxv = torch.empty(rows, dtype=torch.float32, device=dev)
     ws, wsb = _workspace(argmax_workspace_size(rows, vocab), dev, workspace)
     st = lib.ddt_argmax(_ptr(logits), ld, rows, vocab, _ptr(ids), _ptr(maxv), _ptr(ws), wsb,
-                        _stream(stream))
+                        _stream())
     _check("ddt_argmax", st)
     return ids, maxv
 
 
 # ---------------------------------------------------------------- stage 2
+@_on_stream
 def build_tree(topk_logp: torch.Tensor, topk_ids: torch.Tensor, root_token: torch.Tensor,
-               batch: int, L: int, k_tree: int, budget: int, *, out=None, want_score=True,
-               stream=None):
+               batch: int, L: int, k_tree: int, budget: int, *, out=None, want_score=True):
     lib = load()
     _need(topk_logp, torch.float32, "topk_logp")
     _need(topk_ids, torch.int32, "topk_ids")
@@ -257,7 +274,7 @@ def build_tree(topk_logp: torch.Tensor, topk_ids: torch.Tensor, root_token: torc
     st = lib.ddt_build_tree(_ptr(topk_logp), _ptr(topk_ids), _ptr(root_token), batch, L, k,
                             k_tree, budget, _ptr(out["n_nodes"]), _ptr(out["token"]),
                             _ptr(out["parent"]), _ptr(out["depth"]), _ptr(out.get("score")),
-                            _ptr(out["mask"]), None, 0, _stream(stream))
+                            _ptr(out["mask"]), None, 0, _stream())
     _check("ddt_build_tree", st)
     return out
 
@@ -271,11 +288,12 @@ def attention_workspace_size(desc: AttnDesc) -> int:
     return int(load().ddt_masked_attention_workspace_size(ctypes.byref(desc)))
 
 
+@_on_stream
 def masked_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                      kv_base: torch.Tensor, prefix_len: torch.Tensor, n_q: torch.Tensor,
                      own_mask: Optional[torch.Tensor] = None, *, max_kv_len: int,
                      scale: float = 0.0, out=None, lse=None, want_lse=False, workspace=None,
-                     block_len: int = 0, stream=None):
+                     block_len: int = 0):
     """q bf16 [b, n_q_max, hq, D]; k/v bf16 [rows, hkv, D]; own_mask int64
     [b, n_q_max, W] (bit patterns) or None for the dense drafter block.
     block_len > 0 (no mask): packed drafter blocks, each query sees the prefix
@@ -304,23 +322,24 @@ def masked_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
         st = lib.ddt_packed_block_attention(ctypes.byref(desc), int(block_len), _ptr(q),
                                             _ptr(k_cache), _ptr(v_cache), _ptr(kv_base),
                                             _ptr(prefix_len), _ptr(n_q), _ptr(out), _ptr(lse),
-                                            _ptr(ws), wsb, _stream(stream))
+                                            _ptr(ws), wsb, _stream())
         _check("ddt_packed_block_attention", st)
         return (out, lse) if want_lse else out
     st = lib.ddt_masked_attention(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(kv_base), _ptr(prefix_len), _ptr(n_q), _ptr(own_mask),
-                                  _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(stream))
+                                  _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream())
     _check("ddt_masked_attention", st)
     return (out, lse) if want_lse else out
 
 
 # ---------------------------------------------------------------- stage 4
+@_on_stream
 def accept_compact(node_token: torch.Tensor, node_parent: torch.Tensor, n_nodes: torch.Tensor,
                    target: torch.Tensor, L: int, k_cache: Optional[torch.Tensor],
                    v_cache: Optional[torch.Tensor], kv_base: Optional[torch.Tensor],
                    prefix_len: torch.Tensor, *, n_layers: Optional[int] = None,
                    layer_stride: Optional[int] = None, hkv: Optional[int] = None,
-                   head_dim: Optional[int] = None, out=None, stream=None):
+                   head_dim: Optional[int] = None, out=None):
     """k_cache/v_cache bf16 [n_layers, rows, hkv, D] (edited in place) or None."""
     lib = load()
     for t, nm in ((node_token, "node_token"), (node_parent, "node_parent"),
@@ -351,6 +370,6 @@ def accept_compact(node_token: torch.Tensor, node_parent: torch.Tensor, n_nodes:
                                 _ptr(target), batch, L, _ptr(k_cache), _ptr(v_cache),
                                 _ptr(kv_base), _ptr(prefix_len), n_layers, layer_stride, hkv,
                                 head_dim, _ptr(out["accept_len"]), _ptr(out["accepted"]),
-                                _ptr(out["bonus"]), _ptr(out["new_len"]), _stream(stream))
+                                _ptr(out["bonus"]), _ptr(out["new_len"]), _stream())
     _check("ddt_accept_compact", st)
     return out

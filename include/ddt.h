@@ -336,7 +336,9 @@ int ddt_packed_block_attention(const ddt_attn_desc* desc, int block_len, const v
  *   hkv*head_dim elements; request b's tree rows start at kv_base[b] + P.
  * outputs: accept_len, bonus_token, new_len i32 [batch];
  *   accepted_nodes i32 [batch, L+1] (path, then -1)
- * Rows >= new_len of the request are unspecified afterwards.
+ * Rows >= new_len of the request are unspecified afterwards.  Accepted
+ * paths of any length up to L are compacted: more than 1024 path rows are
+ * moved in several register rounds, in increasing path order.
  * Errors: EINVAL if batch < 1, n_max < 1, L < 1, n_layers < 0, hkv < 1,
  *         head_dim < 1, hkv*head_dim not a multiple of 8, or a required
  *         pointer is NULL; EUNSUPPORTED if n_layers > 65535 or the slot

@@ -28,3 +28,14 @@ def gpu():
     from block_diffusion_draft_vocab_amd import ddt
     ddt.load()            # raises loudly if the HIP library is missing
     return torch.device("cuda:0")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the largest errors the parity tests measured (tests/report.py)
+    to the JSON file named by DDT_PARITY_REPORT, when that is set."""
+    path = os.environ.get("DDT_PARITY_REPORT")
+    if not path:
+        return
+    from tests import report
+    if report.ERRORS:
+        report.dump(path)

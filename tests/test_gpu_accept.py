@@ -176,3 +176,51 @@ def test_wide_slot_arrays(gpu):
     assert out["accepted"].cpu().tolist() == [[0, 2, 4, -1, -1]]
     assert np.array_equal(host_bf16_bits(kc), okc)
     assert np.array_equal(host_bf16_bits(vc), ovc)
+
+
+def test_long_path_several_rounds(gpu):
+    """An accepted path of 1100 nodes (more rows than one register round of
+    the compaction holds: 1024 per tensor) whose nodes sit at every other
+    slot, so rows of the first round's sources are the second round's
+    destinations."""
+    plen = 1100
+    n = 2 * plen + 1
+    tok = np.zeros((1, n), np.int32)
+    par = np.full((1, n), -1, np.int32)
+    tgt = np.full((1, n), 3, np.int32)
+    for j in range(1, plen + 1):
+        on, off = 2 * j, 2 * j - 1                     # path node, and a leaf beside it
+        prev = 2 * (j - 1)
+        par[0, on] = prev
+        par[0, off] = prev
+        tok[0, on] = 1000 + j
+        tok[0, off] = 5000 + j
+        tgt[0, prev] = 1000 + j
+    tgt[0, 2 * plen] = 42                              # bonus
+    P = 5
+    k, v = _caches(21, 2, P + n, 1, 64)
+    g = _check(gpu, tok, par, [n], tgt, plen, k, v, [0], [P])
+    assert g["accept_len"][0] == plen and g["bonus"][0] == 42
+
+
+def test_deterministic(gpu):
+    """Two runs on the same inputs give identical outputs and caches."""
+    cfg = synth.CONFIGS[5]
+    case, t = _tree(cfg)
+    y = synth.sample_target_path(case)
+    tgt = np.stack([synth.target_for_tree(t["token"][r], t["parent"][r], t["depth"][r],
+                                          int(t["n_nodes"][r]), y[r], case.off_path[r])
+                    for r in range(cfg.batch)])
+    for r in range(0, cfg.batch, 3):
+        n = int(t["n_nodes"][r])
+        stop = int(np.argmax(t["depth"][r][:n]))
+        tgt[r] = synth.force_path_target(t["token"][r], t["parent"][r], t["depth"][r], n, stop,
+                                         case.off_path[r], cfg.vocab)
+    N = cfg.B + 1
+    prefix = np.full(cfg.batch, 7, np.int32)
+    base = np.arange(cfg.batch, dtype=np.int64) * (7 + N)
+    k, v = _caches(23, 3, int(base[-1]) + 7 + N, cfg.hkv, cfg.D)
+    a = _gpu_accept(gpu, t["token"], t["parent"], t["n_nodes"], tgt, cfg.L, k, v, base, prefix)
+    b = _gpu_accept(gpu, t["token"], t["parent"], t["n_nodes"], tgt, cfg.L, k, v, base, prefix)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key

@@ -3,7 +3,8 @@
 Bar (workload tolerance): max |out_gpu - out_oracle| <= 2e-2 on N(0,1) bf16
 inputs; lse within 2e-2 as well.  Masks come from the oracle's tree build.
 Cases: verify mode at the tiny config and at full workload size (257 tree
-rows over 2048 prefix rows, 32/8/128), the 1025-row / 4096-prefix shape, the ragged 32-request serving batch, drafter mode at both
+rows over 2048 prefix rows, 32/8/128), the 1025-row / 4096-prefix shape,
+every request of the ragged 32-request serving batch, drafter mode at both
 drafter shapes, and edge cases (prefix not a multiple of the tile, empty
 prefix, ragged n_q, head dims 32/64/128, GQA ratios 1..8, chain = causal)."""
 import numpy as np
@@ -16,6 +17,7 @@ from oracle.attention import masked_attention as oracle_attn
 from oracle.logits import topk_logprobs as oracle_topk
 from oracle.tree import ancestor_mask
 from oracle.tree import build_trees as oracle_trees
+from tests import report
 from tests.helpers import bf16_f32, dev_bf16, mask_to_dev
 
 pytestmark = pytest.mark.gpu
@@ -36,13 +38,20 @@ def _gpu_attn(gpu, q_bits, k_bits, v_bits, kv_base, prefix, n_q, mask, max_kv_le
     return out.float().cpu().numpy(), lse.cpu().numpy()
 
 
-def _compare(out, lse, oout, olse, prefix, n_q, rows=None):
+def _compare(out, lse, oout, olse, prefix, n_q, case=None):
+    eo = el = 0.0
     for r in range(len(n_q)):
         n = int(n_q[r])
-        sel = range(n) if rows is None else [i for i in rows if i < n]
-        for i in sel:
+        if n == 0:
+            continue
+        eo = max(eo, float(np.abs(out[r, :n] - oout[r, :n]).max()))
+        el = max(el, float(np.abs(lse[r, :n] - olse[r, :n]).max()))
+        for i in range(n):
             assert np.abs(out[r, i] - oout[r, i]).max() <= TOL, (r, i)
             assert np.abs(lse[r, i] - olse[r, i]).max() <= TOL, (r, i)
+    if case is not None:
+        report.record(case, "attn_out_max_abs", eo, TOL)
+        report.record(case, "attn_lse_max_abs", el, TOL)
 
 
 def _tree_masks(cfg, case):
@@ -61,7 +70,7 @@ def test_verify_tiny(gpu):
     oout, olse = oracle_attn(bf16_f32(case.vq_bits), bf16_f32(case.vk_bits),
                              bf16_f32(case.vv_bits), case.kv_base, case.prefix_len, n_q,
                              t["mask"])
-    _compare(out, lse, oout, olse, case.prefix_len, n_q)
+    _compare(out, lse, oout, olse, case.prefix_len, n_q, "verify_c1")
 
 
 @pytest.mark.parametrize("cfg", [synth.CONFIGS[3], synth.DEEP], ids=["c3", "deep"])
@@ -75,7 +84,7 @@ def test_verify_full_size(gpu, cfg):
     oout, olse = oracle_attn(bf16_f32(case.vq_bits), bf16_f32(case.vk_bits),
                              bf16_f32(case.vv_bits), case.kv_base, case.prefix_len, n_q,
                              t["mask"])
-    _compare(out, lse, oout, olse, case.prefix_len, n_q)
+    _compare(out, lse, oout, olse, case.prefix_len, n_q, f"verify_{cfg.name}")
 
 
 @pytest.mark.parametrize("cfg", [synth.CONFIGS[4], synth.FLAT4], ids=["c4", "c4flat"])
@@ -91,7 +100,7 @@ def test_verify_large_budget(gpu, cfg):
     oout, olse = oracle_attn(bf16_f32(case.vq_bits), bf16_f32(case.vk_bits),
                              bf16_f32(case.vv_bits), case.kv_base, case.prefix_len, n_q,
                              t["mask"])
-    _compare(out, lse, oout, olse, case.prefix_len, n_q)
+    _compare(out, lse, oout, olse, case.prefix_len, n_q, f"verify_{cfg.name}")
 
 
 def test_serving_ragged_batch(gpu):
@@ -102,15 +111,20 @@ def test_serving_ragged_batch(gpu):
     n_q = np.full(cfg.batch, N, np.int32)
     out, lse = _gpu_attn(gpu, case.vq_bits, case.vk_bits, case.vv_bits, case.kv_base,
                          case.prefix_len, n_q, t["mask"], int(case.prefix_len.max()) + N)
-    reqs = [int(np.argmin(case.prefix_len)), int(np.argmax(case.prefix_len)), 3, 17]
+    # every request against the oracle, one request at a time (its own rows)
     k = bf16_f32(case.vk_bits)
     v = bf16_f32(case.vv_bits)
     q = bf16_f32(case.vq_bits)
-    for r in reqs:
+    eo = el = 0.0
+    for r in range(cfg.batch):
         oout, olse = oracle_attn(q[r:r + 1], k, v, case.kv_base[r:r + 1],
                                  case.prefix_len[r:r + 1], n_q[r:r + 1], t["mask"][r:r + 1])
+        eo = max(eo, float(np.abs(out[r, :N] - oout[0]).max()))
+        el = max(el, float(np.abs(lse[r, :N] - olse[0]).max()))
         assert np.abs(out[r, :N] - oout[0]).max() <= TOL, r
         assert np.abs(lse[r, :N] - olse[0]).max() <= TOL, r
+    report.record("verify_serving_b32", "attn_out_max_abs", eo, TOL)
+    report.record("verify_serving_b32", "attn_lse_max_abs", el, TOL)
 
 
 @pytest.mark.parametrize("cfg", [synth.CONFIGS[1], synth.CONFIGS[2]], ids=["c1", "c2"])
@@ -125,7 +139,7 @@ def test_drafter_mode(gpu, cfg):
                          None, ctx + L)
     oout, olse = oracle_attn(bf16_f32(case.dq_bits), bf16_f32(case.dk_bits),
                              bf16_f32(case.dv_bits), kv_base, prefix, n_q, None)
-    _compare(out, lse, oout, olse, prefix, n_q)
+    _compare(out, lse, oout, olse, prefix, n_q, f"drafter_{cfg.name}")
 
 
 def _rand_case(seed, b, nq_max, n_q, prefix, hq, hkv, D):
@@ -163,7 +177,7 @@ def test_edge_shapes(gpu, D, hq, hkv, prefix, n_q, nq_max, masked):
     max_kv = int(max(p + n for p, n in zip(prefix, n_q)))
     out, lse = _gpu_attn(gpu, q, k, v, base, prefix, n_q, mask, max_kv)
     oout, olse = oracle_attn(bf16_f32(q), bf16_f32(k), bf16_f32(v), base, prefix, n_q, mask)
-    _compare(out, lse, oout, olse, prefix, n_q)
+    _compare(out, lse, oout, olse, prefix, n_q, "edge_shapes")
 
 
 def test_rows_beyond_n_q_untouched(gpu):

@@ -89,3 +89,47 @@ def test_padding_slots_untouched():
     assert pos[0].tolist() == [30, 31, 31, 32, -1, -1]
     assert np.array_equal(q2[0, 4:], q[0, 4:])
     assert np.all(kc2[34:] == 0) and np.all(kc2[:30] == 0)
+
+
+def _torch_bf16_bits(x64):
+    import torch
+    t = torch.from_numpy(np.asarray(x64, dtype=np.float64)).float().bfloat16()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rounding_matches_torch():
+    """The oracle's final rounding (float64 -> float32 -> bf16, nearest-even
+    both times) equals torch's CPU conversions on random values of every
+    magnitude, on exact bf16 ties (float32 low half 0x8000, even and odd
+    upper halves, both signs), just off the ties, on float64 values that
+    only become a tie after the float32 step, on subnormals and signed
+    zeros, and at the top of the float32 range (rounds to infinity)."""
+    from oracle.rope import _f64_to_bf16_bits
+    rng = np.random.default_rng(11)
+    vals = [rng.standard_normal(4000) * 10.0 ** rng.integers(-30, 30, 4000)]
+    hi = rng.integers(0, 0x7F7F, 2000, dtype=np.uint32) << 16
+    for low in (0x8000, 0x7FFF, 0x8001, 0x0000, 0xFFFF):
+        u = (hi | np.uint32(low)).astype(np.uint32)
+        f = u.view(np.float32).astype(np.float64)
+        vals += [f, -f]
+    # float64 just above / below a float32 tie: the float32 step decides
+    ties = ((hi | np.uint32(0x8000)).astype(np.uint32)).view(np.float32).astype(np.float64)
+    vals += [np.nextafter(ties, np.inf), np.nextafter(ties, -np.inf)]
+    vals += [np.array([0.0, -0.0, 1e-45, -1e-45, 1e-39, 3.4028234663852886e38,
+                       -3.4028234663852886e38, 3.3961775292304e38, 1.0, -1.0])]
+    x = np.concatenate(vals)
+    assert np.array_equal(_f64_to_bf16_bits(x), _torch_bf16_bits(x))
+    # the worked tie cases, by hand: 1 + 2^-8 is halfway between bf16 1 and
+    # 1 + 2^-7 and goes to the even one (1.0); 1 + 3 * 2^-8 goes up to 1 + 2^-6
+    assert _f64_to_bf16_bits(np.array([1 + 2.0 ** -8]))[0] == 0x3F80
+    assert _f64_to_bf16_bits(np.array([1 + 3 * 2.0 ** -8]))[0] == 0x3F82
+
+
+def test_bf16_input_generator_matches_torch():
+    """The seeded generators' bf16 storage rounding (float32 -> bf16) equals
+    torch's, so both sides of every parity test read the values torch would."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-20, 20, 20000)).astype(np.float32)
+    u = rng.integers(0, 0x7F7F, 2000, dtype=np.uint32) << 16 | np.uint32(0x8000)
+    x = np.concatenate([x, u.astype(np.uint32).view(np.float32)])
+    assert np.array_equal(synth.f32_to_bf16_bits(x), _torch_bf16_bits(x.astype(np.float64)))
