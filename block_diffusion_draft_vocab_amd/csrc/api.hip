@@ -55,6 +55,23 @@ DDT_EXPORT int ddt_topk_logprobs(const float* logits, int64_t ld_logits, int n_r
                                         static_cast<hipStream_t>(stream)));
 }
 
+DDT_EXPORT int ddt_topk_logprobs_noalloc(const float* logits, int64_t ld_logits, int n_rows,
+                                         int vocab, int k, float inv_temperature,
+                                         int32_t* topk_ids, float* topk_logp, float* lse,
+                                         void* stream) {
+  if (!topk_args_ok(n_rows, vocab, k) || ld_logits < vocab) return DDT_EINVAL;
+  if (logits == nullptr || topk_ids == nullptr || topk_logp == nullptr) return DDT_EINVAL;
+  if (!(inv_temperature > 0.f) || !isfinite(inv_temperature)) return DDT_EINVAL;
+  if (!ddt::topk_supported(n_rows, vocab, k)) return DDT_EUNSUPPORTED;
+  if (ddt::topk_workspace_bytes(n_rows, vocab, k) > DDT_TOPK_NOALLOC_SCRATCH_BYTES)
+    return DDT_EWORKSPACE;
+  void* scratch = nullptr;
+  if (ddt::topk_noalloc_scratch(&scratch) != hipSuccess) return DDT_ELAUNCH;
+  return launch_status(ddt::launch_topk(logits, ld_logits, n_rows, vocab, k, inv_temperature,
+                                        topk_ids, topk_logp, lse, scratch,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 // ---- fused LM head + log-softmax / top-K ------------------------------------
 static bool lmhead_args_ok(int n_rows, int hidden, int vocab, int k) {
   return n_rows >= 1 && hidden >= 1 && vocab >= 1 && k >= 1 && k <= vocab;

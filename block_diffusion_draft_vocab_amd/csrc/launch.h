@@ -23,6 +23,9 @@ size_t topk_workspace_bytes(int n_rows, int vocab, int k);
 hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, int k,
                        float inv_t, int32_t* ids, float* logp, float* lse, void* ws,
                        hipStream_t stream);
+// Device address of the allocation-free top-K entry point's scratch array on
+// the current device (looked up once per device, nothing allocated).
+hipError_t topk_noalloc_scratch(void** ptr);
 
 // Merge of per-chunk partials (sorted key lists + (max, sum of exp)) into
 // the rows' top-k ids / log-probs / lse; shared by the logit pass and the

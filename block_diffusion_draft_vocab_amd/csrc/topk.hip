@@ -24,8 +24,10 @@
 // key is a larger x and, among equal x, a smaller id.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
+#include "../../include/ddt.h"
 #include "common.h"
 #include "launch.h"
 
@@ -564,6 +566,33 @@ bool topk_supported(int n_rows, int vocab, int k) {
   const TopkPlan p = topk_plan(n_rows, vocab, k);
   return n_rows <= 65535 && p.chunk_len <= kTopkMaxChunk && p.n_chunks <= kTopkPlanMaxLists &&
          p.n_chunks * k <= 8192;
+}
+
+namespace {
+// Partials of the allocation-free entry point: one array per GPU, zero at
+// load and never cleared (the partial kernel writes every entry the merge
+// reads).  Host code must not pass this name to a kernel: on the host it is
+// only a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[DDT_TOPK_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t topk_noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // with device dev current: that device's copy of the array
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 hipError_t launch_topk(const float* logits, int64_t ld, int n_rows, int vocab, int k,

@@ -32,6 +32,7 @@ SIGNATURES = {
     "ddt_status_string": (_c.c_char_p, [_I]),
     "ddt_topk_logprobs_workspace_size": (_SZ, [_I, _I, _I]),
     "ddt_topk_logprobs": (_I, [_P, _I64, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
+    "ddt_topk_logprobs_noalloc": (_I, [_P, _I64, _I, _I, _I, _F, _P, _P, _P, _P]),
     "ddt_lmhead_topk_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "ddt_lmhead_topk": (_I, [_P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P]),
     "ddt_tree_rope_kv": (_I, [_P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _P,
@@ -152,6 +153,31 @@ def topk_logprobs(logits: torch.Tensor, k: int, inv_temperature: float = 1.0, *,
     st = lib.ddt_topk_logprobs(_ptr(logits), ld, rows, vocab, k, float(inv_temperature),
                                _ptr(ids), _ptr(logp), _ptr(lse), _ptr(ws), wsb, _stream())
     _check("ddt_topk_logprobs", st)
+    return ids, logp, lse
+
+
+@_on_stream
+def topk_logprobs_noalloc(logits: torch.Tensor, k: int, inv_temperature: float = 1.0, *,
+                          vocab: Optional[int] = None, ids=None, logp=None, lse=None,
+                          want_lse: bool = True):
+    """topk_logprobs through ddt_topk_logprobs_noalloc: the library's own
+    per-device scratch instead of a workspace (outputs still allocated here
+    unless given)."""
+    lib = load()
+    if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_cuda:
+        raise ValueError("logits must be a device float32 [rows, ld] tensor")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    rows, ld = logits.shape[0], logits.stride(0)
+    vocab = logits.shape[1] if vocab is None else vocab
+    dev = logits.device
+    ids = torch.empty(rows, k, dtype=torch.int32, device=dev) if ids is None else ids
+    logp = torch.empty(rows, k, dtype=torch.float32, device=dev) if logp is None else logp
+    if want_lse and lse is None:
+        lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    st = lib.ddt_topk_logprobs_noalloc(_ptr(logits), ld, rows, vocab, k, float(inv_temperature),
+                                       _ptr(ids), _ptr(logp), _ptr(lse), _stream())
+    _check("ddt_topk_logprobs_noalloc", st)
     return ids, logp, lse
 
 

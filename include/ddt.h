@@ -91,6 +91,29 @@ int ddt_topk_logprobs(const float* logits, int64_t ld_logits, int n_rows, int vo
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Stage 1 without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Same definition, arguments, outputs and errors as ddt_topk_logprobs; the
+ * per-chunk partials go to a scratch array that the library holds in device
+ * memory of each GPU it runs on (DDT_TOPK_NOALLOC_SCRATCH_BYTES, held until
+ * the process ends).  The call allocates nothing.  Its first call on a
+ * device looks up that device's scratch address (no allocation; make it
+ * outside graph capture).
+ * Extra error: EWORKSPACE if the shape needs more scratch than
+ *   DDT_TOPK_NOALLOC_SCRATCH_BYTES (ddt_topk_logprobs_workspace_size() tells
+ *   how much), ELAUNCH if the scratch address cannot be looked up.
+ * Every call on one GPU uses that GPU's one scratch array: calls that
+ * overlap on one GPU (concurrent streams, threads) race and must not be
+ * issued; calls in one stream are ordered and safe.
+ * ---------------------------------------------------------------------- */
+#define DDT_TOPK_NOALLOC_SCRATCH_BYTES (8u << 20)
+int ddt_topk_logprobs_noalloc(const float* logits, int64_t ld_logits, int n_rows, int vocab,
+                              int k, float inv_temperature, int32_t* topk_ids,
+                              float* topk_logp, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
  * Fused LM head + log-softmax / top-K (stage 1 fed from hidden states).
  *
  * [DFlash] "임베딩과 출력 헤드는 공유한다" (embedding and output head are

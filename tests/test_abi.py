@@ -29,7 +29,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(ddt.SIGNATURES)
@@ -40,6 +40,30 @@ def test_exports_every_declared_symbol(lib):
 def _topk(lib, logits=FAKE, ld=1000, rows=4, V=1000, k=4, inv_t=1.0, ids=FAKE, logp=FAKE,
           ws=FAKE, wsb=1 << 30):
     return lib.ddt_topk_logprobs(logits, ld, rows, V, k, inv_t, ids, logp, None, ws, wsb, None)
+
+
+def _topk_noalloc(lib, logits=FAKE, ld=1000, rows=4, V=1000, k=4, inv_t=1.0, ids=FAKE,
+                  logp=FAKE):
+    return lib.ddt_topk_logprobs_noalloc(logits, ld, rows, V, k, inv_t, ids, logp, None, None)
+
+
+def test_topk_noalloc_validation(lib):
+    """Host-side checks of the allocation-free top-K (nothing is launched):
+    the stage-1 argument rules, and shapes whose partials would not fit the
+    library's scratch array are refused with EWORKSPACE."""
+    E = ddt
+    assert _topk_noalloc(lib, logits=None) == E.DDT_EINVAL
+    assert _topk_noalloc(lib, logp=None) == E.DDT_EINVAL
+    assert _topk_noalloc(lib, k=129) == E.DDT_EINVAL
+    assert _topk_noalloc(lib, ld=999) == E.DDT_EINVAL
+    assert _topk_noalloc(lib, inv_t=-1.0) == E.DDT_EINVAL
+    assert _topk_noalloc(lib, rows=70000, ld=151936, V=151936, k=16) == E.DDT_EUNSUPPORTED
+    # 8000 rows x 19 chunks x 16 keys x 8 B = 19.5 MB of partials > 8 MiB
+    need = lib.ddt_topk_logprobs_workspace_size(8000, 151936, 16)
+    assert need > (8 << 20)
+    assert _topk_noalloc(lib, rows=8000, ld=151936, V=151936, k=16) == E.DDT_EWORKSPACE
+    # the largest serving batch of the workloads fits
+    assert lib.ddt_topk_logprobs_workspace_size(512, 151936, 16) <= (8 << 20)
 
 
 def test_topk_validation(lib):
