@@ -54,6 +54,11 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="launch every stage from Python instead of replaying one HIP graph "
                          "per input set")
+    ap.add_argument("--stage-replays", type=int, default=50,
+                    help="replays of each per-stage graph (and of the step graph) timed one "
+                         "by one for the per-stage times and their spread")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the budget-1024 and serving-batch chain steps")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--no-streams", action="store_true",
                     help="skip the extra logit-stream measurements (target argmax over the "
@@ -306,13 +311,58 @@ def log(args, msg):
         print(msg, file=sys.stderr, flush=True)
 
 
-class Step:
-    """Device buffers for one input set plus the preallocated outputs."""
+def replay_times(torch, g, reps):
+    """Device time of each of reps replays of graph g (ms): HIP events on the
+    launch stream between consecutive replays."""
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        g.replay()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
 
-    def __init__(self, case, dev, torch, ddt):
+
+def capture(torch, fns):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    return g
+
+
+def warm_on_side_stream(torch, fns):
+    """Run fns once on a side stream (allocator warm-up before capture)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+
+
+def spread(per_launch_ms):
+    """(mean, median, min) in microseconds."""
+    a = np.asarray(per_launch_ms) * 1e3
+    return float(a.mean()), float(np.median(a)), float(a.min())
+
+
+class Chain:
+    """Device buffers and the stage calls of one input set of a workload:
+    drafter attention (when the workload has a drafter pass), top-K, tree,
+    verify attention, acceptance + compaction of one layer.  Workspaces are
+    shared by all sets of the workload (ws dict)."""
+
+    NAMES = ["drafter_attn", "topk", "tree", "verify_attn", "accept"]
+
+    def __init__(self, case, dev, torch, ddt, ws, max_kv):
         cfg = case.cfg
-        self.cfg = cfg
-        L, N, ctx = cfg.L, cfg.B + 1, cfg.drafter_ctx
+        self.cfg, self.case, self.ddt, self.ws, self.max_kv = cfg, case, ddt, ws, max_kv
+        b, L, N, ctx = cfg.batch, cfg.L, cfg.B + 1, cfg.drafter_ctx
 
         def bf16(bits):
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
@@ -320,36 +370,206 @@ class Step:
 
         self.logits = torch.from_numpy(case.logits).to(dev)
         self.root = torch.from_numpy(case.root_token).to(dev)
-        self.dq, self.dk, self.dv = bf16(case.dq_bits), bf16(case.dk_bits), bf16(case.dv_bits)
-        self.d_base = torch.zeros(1, dtype=torch.int64, device=dev)
-        self.d_prefix = torch.full((1,), ctx, dtype=torch.int32, device=dev)
-        self.d_nq = torch.full((1,), L, dtype=torch.int32, device=dev)
+        self.has_drafter = ctx > 0 and case.dq_bits is not None
+        if self.has_drafter:
+            self.dq, self.dk, self.dv = (bf16(case.dq_bits), bf16(case.dk_bits),
+                                         bf16(case.dv_bits))
+            self.d_base = torch.arange(b, dtype=torch.int64, device=dev) * (ctx + L)
+            self.d_prefix = torch.full((b,), ctx, dtype=torch.int32, device=dev)
+            self.d_nq = torch.full((b,), L, dtype=torch.int32, device=dev)
+            self.d_out = torch.empty_like(self.dq)
         self.vq, self.vk, self.vv = bf16(case.vq_bits), bf16(case.vk_bits), bf16(case.vv_bits)
         self.kv_base = torch.from_numpy(case.kv_base).to(dev)
         self.prefix = torch.from_numpy(case.prefix_len).to(dev)
         self.kc = self.vk[None]          # one layer, compacted in place
         self.vc = self.vv[None]
-        self.d_out = torch.empty_like(self.dq)
         self.v_out = torch.empty_like(self.vq)
-        self.ids = torch.empty(L, cfg.K, dtype=torch.int32, device=dev)
-        self.logp = torch.empty(L, cfg.K, dtype=torch.float32, device=dev)
-        self.lse = torch.empty(L, dtype=torch.float32, device=dev)
+        self.ids = torch.empty(b * L, cfg.K, dtype=torch.int32, device=dev)
+        self.logp = torch.empty(b * L, cfg.K, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(b * L, dtype=torch.float32, device=dev)
         W = (N + 63) // 64
         self.tree = {
-            "n_nodes": torch.empty(1, dtype=torch.int32, device=dev),
-            "token": torch.empty(1, N, dtype=torch.int32, device=dev),
-            "parent": torch.empty(1, N, dtype=torch.int32, device=dev),
-            "depth": torch.empty(1, N, dtype=torch.int32, device=dev),
-            "score": torch.empty(1, N, dtype=torch.float32, device=dev),
-            "mask": torch.empty(1, N, W, dtype=torch.int64, device=dev),
+            "n_nodes": torch.empty(b, dtype=torch.int32, device=dev),
+            "token": torch.empty(b, N, dtype=torch.int32, device=dev),
+            "parent": torch.empty(b, N, dtype=torch.int32, device=dev),
+            "depth": torch.empty(b, N, dtype=torch.int32, device=dev),
+            "score": torch.empty(b, N, dtype=torch.float32, device=dev),
+            "mask": torch.empty(b, N, W, dtype=torch.int64, device=dev),
         }
         self.acc = {
-            "accept_len": torch.empty(1, dtype=torch.int32, device=dev),
-            "accepted": torch.empty(1, L + 1, dtype=torch.int32, device=dev),
-            "bonus": torch.empty(1, dtype=torch.int32, device=dev),
-            "new_len": torch.empty(1, dtype=torch.int32, device=dev),
+            "accept_len": torch.empty(b, dtype=torch.int32, device=dev),
+            "accepted": torch.empty(b, L + 1, dtype=torch.int32, device=dev),
+            "bonus": torch.empty(b, dtype=torch.int32, device=dev),
+            "new_len": torch.empty(b, dtype=torch.int32, device=dev),
         }
         self.target = None
+        self.verify_flops = None
+
+    def stage_calls(self):
+        """[(name, fn)] of one step, in chain order."""
+        ddt, cfg, ws = self.ddt, self.cfg, self.ws
+        L, ctx = cfg.L, cfg.drafter_ctx
+        out = []
+        if self.has_drafter:
+            out.append(("drafter_attn", lambda: ddt.masked_attention(
+                self.dq, self.dk, self.dv, self.d_base, self.d_prefix, self.d_nq, None,
+                max_kv_len=ctx + L, out=self.d_out, workspace=ws["attn_d"])))
+        out += [
+            ("topk", lambda: ddt.topk_logprobs(self.logits, cfg.K, cfg.inv_temperature,
+                                               ids=self.ids, logp=self.logp, lse=self.lse,
+                                               workspace=ws["topk"])),
+            ("tree", lambda: ddt.build_tree(self.logp, self.ids, self.root, cfg.batch, L,
+                                            cfg.k_tree, cfg.B, out=self.tree)),
+            ("verify_attn", lambda: ddt.masked_attention(
+                self.vq, self.vk, self.vv, self.kv_base, self.prefix, self.tree["n_nodes"],
+                self.tree["mask"], max_kv_len=self.max_kv, out=self.v_out,
+                workspace=ws["attn_v"])),
+            ("accept", lambda: ddt.accept_compact(
+                self.tree["token"], self.tree["parent"], self.tree["n_nodes"], self.target, L,
+                self.kc, self.vc, self.kv_base, self.prefix, out=self.acc)),
+        ]
+        return out
+
+    def prepare(self, torch, synth, dev):
+        """Run the stages up to the tree once, then draw the synthetic
+        target's greedy tokens along the tree they built (host-side input
+        generation, outside every timed region), and count the verify FLOPs
+        (keys each tree row can see)."""
+        for name, f in self.stage_calls():
+            if name in ("drafter_attn", "topk", "tree"):
+                f()
+        torch.cuda.synchronize()
+        cfg, case = self.cfg, self.case
+        tok = self.tree["token"].cpu().numpy()
+        par = self.tree["parent"].cpu().numpy()
+        dep = self.tree["depth"].cpu().numpy()
+        nn = self.tree["n_nodes"].cpu().numpy()
+        y = synth.sample_target_path(case)
+        self.target = torch.from_numpy(np.stack([
+            synth.target_for_tree(tok[r], par[r], dep[r], int(nn[r]), y[r], case.off_path[r])
+            for r in range(cfg.batch)])).to(dev)
+        vis = sum(int(nn[r]) * int(case.prefix_len[r]) + int((dep[r, :nn[r]] + 1).sum())
+                  for r in range(cfg.batch))
+        self.verify_flops = 4.0 * cfg.D * cfg.hq * vis
+        self.depths = [dep[r, :nn[r]].astype(np.int64) for r in range(cfg.batch)]
+
+
+def chain_workspaces(torch, ddt, cfg, max_kv, dev):
+    L, N, ctx, b = cfg.L, cfg.B + 1, cfg.drafter_ctx, cfg.batch
+    ws = {}
+    if ctx > 0:
+        d = ddt.attn_desc(b, cfg.hq, cfg.hkv, cfg.D, L, ctx + L)
+        ws["attn_d"] = torch.empty(max(1, ddt.attention_workspace_size(d)), dtype=torch.uint8,
+                                   device=dev)
+    v = ddt.attn_desc(b, cfg.hq, cfg.hkv, cfg.D, N, max_kv, (N + 63) // 64)
+    ws["attn_v"] = torch.empty(max(1, ddt.attention_workspace_size(v)), dtype=torch.uint8,
+                               device=dev)
+    ws["topk"] = torch.empty(ddt.topk_workspace_size(b * L, cfg.vocab, cfg.K),
+                             dtype=torch.uint8, device=dev)
+    return ws
+
+
+def make_chains(args, torch, ddt, synth, cfg, n_sets, seed0, dev):
+    cases = [synth.make_case(cfg, seed=seed0 + 1000 * i) for i in range(n_sets)]
+    max_kv = max(int(c.prefix_len.max()) for c in cases) + cfg.B + 1
+    ws = chain_workspaces(torch, ddt, cfg, max_kv, dev)
+    chains = [Chain(c, dev, torch, ddt, ws, max_kv) for c in cases]
+    for ch in chains:
+        ch.prepare(torch, synth, dev)
+    return cases, chains
+
+
+def time_stages(torch, chains, reps):
+    """Per-stage device time: one graph per stage holds that stage for every
+    input set back to back and is replayed reps times, a HIP event between
+    replays.  Returns {stage: per-launch ms of each replay}."""
+    names = [n for n, _ in chains[0].stage_calls()]
+    per = {}
+    for j, name in enumerate(names):
+        g = capture(torch, [ch.stage_calls()[j][1] for ch in chains])
+        per[name] = replay_times(torch, g, reps) / len(chains)
+        del g
+    return per
+
+
+def stage_summary(per):
+    out = {}
+    for name, a in per.items():
+        mean, med, mn = spread(a)
+        out[name] = {"mean": round(mean, 3), "median": round(med, 3), "min": round(mn, 3)}
+    return out
+
+
+def workload_leg(args, torch, ddt, synth, cfg, n_sets, seed0, dev, label, reps):
+    """A whole chain step of one more workload (budget 1024 peaked / flat, the
+    32-request serving batch): steps/s from graphs of n_sets steps replayed
+    reps times, per-stage times, verify attention and tree against their
+    bounds."""
+    log(args, f"{label}: generating {n_sets} input sets")
+    cases, chains = make_chains(args, torch, ddt, synth, cfg, n_sets, seed0, dev)
+    fns = [f for ch in chains for _, f in ch.stage_calls()]
+    warm_on_side_stream(torch, fns)
+    g = capture(torch, fns)
+    step_ms = replay_times(torch, g, reps) / n_sets
+    del g
+    per = time_stages(torch, chains, reps)
+    st = stage_summary(per)
+    fl = float(np.mean([ch.verify_flops for ch in chains]))
+    tv = st["verify_attn"]["mean"] * 1e-6
+    b, L = cfg.batch, cfg.L
+    lb = b * L * cfg.vocab * 4 + b * L * cfg.K * 8 + b * L * 4
+    tl = st["topk"]["mean"] * 1e-6
+    mean, med, mn = spread(step_ms)
+    res = {
+        "workload": label, "steps_per_s": round(1e3 / (mean * 1e-3), 2),
+        "us_per_step": {"mean": round(mean, 3), "median": round(med, 3), "min": round(mn, 3)},
+        "replays": reps, "input_sets": n_sets, "stages_us": st,
+        "verify_attn": {"bound": "mfma", "algorithmic_flops": fl, "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "achieved": round(fl / tv / 1e12, 1),
+                        "frac": round(fl / tv / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "logit_pass": {"bound": "hbm", "algorithmic_bytes": lb, "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "achieved": round(lb / tl / 1e9, 1),
+                       "frac": round(lb / tl / 1e9 / HBM_PEAK_GBS, 4)},
+        "mean_tree_depth_max": round(float(np.mean([max(int(d.max()) for d in ch.depths)
+                                                    for ch in chains])), 2),
+        "mean_accept_len": None,
+    }
+    torch.cuda.synchronize()
+    res["mean_accept_len"] = round(float(np.mean([ch.acc["accept_len"].float().mean().item()
+                                                  for ch in chains])), 3)
+    del chains, cases
+    torch.cuda.empty_cache()
+    return res
+
+
+def floor_leg(torch, ddt, dev, reps):
+    """What one launch costs on this GPU, with this library's simplest kernel
+    (ddt_argmax over rows of at most one 8192-float chunk: a single launch,
+    one read of the input, no merge): 20 dependent launches of a 1 x 64 row
+    in one graph (the per-launch floor of back-to-back kernels), and 20
+    launches that each read 9.73 MB, the logit pass's byte count, in two grid
+    shapes (297 x 8192 and 1188 x 2048 floats)."""
+    out = {}
+    tiny = torch.zeros(1, 64, dtype=torch.float32, device=dev)
+    ids = torch.empty(1, dtype=torch.int32, device=dev)
+    fns = [lambda: ddt.argmax(tiny, ids=ids) for _ in range(20)]
+    warm_on_side_stream(torch, fns)
+    g = capture(torch, fns)
+    out["dependent_launch_us"] = round(spread(replay_times(torch, g, reps) / 20)[0], 3)
+    best = None
+    for rows, V in ((297, 8192), (1188, 2048)):
+        bufs = [torch.randn(rows, V, device=dev) for _ in range(4)]
+        oid = torch.empty(rows, dtype=torch.int32, device=dev)
+        fns = [lambda b=b: ddt.argmax(b, ids=oid) for b in bufs] * 5
+        warm_on_side_stream(torch, fns)
+        g = capture(torch, fns)
+        t = spread(replay_times(torch, g, reps) / 20)[0]
+        out[f"one_launch_read_us_{rows}x{V}"] = round(t, 3)
+        best = t if best is None else min(best, t)
+        del bufs, g
+    out["one_launch_read_us"] = round(best, 3)
+    out["read_bytes"] = 297 * 8192 * 4
+    return out
 
 
 def main():
@@ -373,52 +593,12 @@ def main():
     L, N, K, B = cfg.L, cfg.B + 1, cfg.K, cfg.B
     ctx, P = cfg.drafter_ctx, cfg.prefix[0]
     log(args, f"generating {args.sets} input sets")
-    cases = [synth.make_case(cfg, seed=args.seed + 1000 * i) for i in range(args.sets)]
-    steps = [Step(c, dev, torch, ddt) for c in cases]
-
-    d_desc = ddt.attn_desc(1, cfg.hq, cfg.hkv, cfg.D, L, ctx + L)
-    v_desc = ddt.attn_desc(1, cfg.hq, cfg.hkv, cfg.D, N, P + N, (N + 63) // 64)
-    ws_attn_d = torch.empty(max(1, ddt.attention_workspace_size(d_desc)), dtype=torch.uint8,
-                            device=dev)
-    ws_attn_v = torch.empty(max(1, ddt.attention_workspace_size(v_desc)), dtype=torch.uint8,
-                            device=dev)
-    ws_topk = torch.empty(ddt.topk_workspace_size(L, cfg.vocab, K), dtype=torch.uint8,
-                          device=dev)
-
-    def stage_calls(s: Step):
-        return [
-            lambda: ddt.masked_attention(s.dq, s.dk, s.dv, s.d_base, s.d_prefix, s.d_nq, None,
-                                         max_kv_len=ctx + L, out=s.d_out, workspace=ws_attn_d),
-            lambda: ddt.topk_logprobs(s.logits, K, 1.0, ids=s.ids, logp=s.logp, lse=s.lse,
-                                      workspace=ws_topk),
-            lambda: ddt.build_tree(s.logp, s.ids, s.root, 1, L, cfg.k_tree, B, out=s.tree),
-            lambda: ddt.masked_attention(s.vq, s.vk, s.vv, s.kv_base, s.prefix,
-                                         s.tree["n_nodes"], s.tree["mask"], max_kv_len=P + N,
-                                         out=s.v_out, workspace=ws_attn_v),
-            lambda: ddt.accept_compact(s.tree["token"], s.tree["parent"], s.tree["n_nodes"],
-                                       s.target, L, s.kc, s.vc, s.kv_base, s.prefix,
-                                       out=s.acc),
-        ]
-
-    # synthetic target "argmax" per set, along the tree this chain builds
-    depths = []
-    for s, c in zip(steps, cases):
-        for f in stage_calls(s)[:3]:
-            f()
-        torch.cuda.synchronize()
-        tok = s.tree["token"].cpu().numpy()[0]
-        par = s.tree["parent"].cpu().numpy()[0]
-        dep = s.tree["depth"].cpu().numpy()[0]
-        n = int(s.tree["n_nodes"].item())
-        y = synth.sample_target_path(c)[0]
-        s.target = torch.from_numpy(
-            synth.target_for_tree(tok, par, dep, n, y, c.off_path[0])[None]).to(dev)
-        depths.append(dep[:n].astype(np.int64))
-    calls = [stage_calls(s) for s in steps]
-    names = ["drafter_attn", "topk", "tree", "verify_attn", "accept"]
-
+    cases, chains = make_chains(args, torch, ddt, synth, cfg, args.sets, args.seed, dev)
+    calls = [[f for _, f in ch.stage_calls()] for ch in chains]
+    names = Chain.NAMES
     stream = torch.cuda.current_stream()
     G = 1
+    reps_b = max(args.stage_replays, 1)
     if args.eager:
         log(args, f"warmup {args.warmup}")
         for i in range(args.warmup):
@@ -438,29 +618,16 @@ def main():
                 e[j + 1].record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        per = {n: np.array([e[j].elapsed_time(e[j + 1]) for e in ev])
+               for j, n in enumerate(names)}
     else:
-        # region A: one HIP graph per input set holds the whole step
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for c in calls:
-                for f in c:
-                    f()
-        torch.cuda.synchronize()
-
-        def capture(fns):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for f in fns:
-                    f()
-            return g
-
-        # G consecutive steps (input sets i..i+G-1) per graph; single-step
-        # graphs cover a remainder, so exactly --steps steps run
+        # region A: HIP graphs of G consecutive steps (one per input set);
+        # single-step graphs cover a remainder, so exactly --steps steps run
+        warm_on_side_stream(torch, [f for c in calls for f in c])
         G = max(1, min(args.graph_sets, len(calls)))
-        multi = [capture([f for c in calls[i:i + G] for f in c])
+        multi = [capture(torch, [f for c in calls[i:i + G] for f in c])
                  for i in range(0, len(calls) - G + 1, G)]
-        single = [capture(c) for c in calls]
+        single = [capture(torch, c) for c in calls]
         log(args, f"warmup {args.warmup}")
         for i in range(args.warmup):
             single[i % len(single)].replay()
@@ -473,29 +640,15 @@ def main():
             single[i % len(single)].replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        # region B: per-stage device time.  One graph per stage holds that
-        # stage for every input set back to back; HIP events on the launch
-        # stream bracket each replay (events cannot be timed inside a
-        # captured graph here), so a launch's average duration includes the
-        # small gap between kernels of one graph.
-        stage_graphs = [capture([c[j] for c in calls]) for j in range(len(names))]
-        reps = max(1, min(args.steps, 1000) // len(calls))
-        ev = []
-        for j, g in enumerate(stage_graphs):
-            for _ in range(3):
-                g.replay()
-            torch.cuda.synchronize()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(reps):
-                g.replay()
-            b.record(stream)
-            ev.append((a, b))
-        torch.cuda.synchronize()
-        log(args, f"timed {reps} replays of {len(calls)} launches per stage")
-        # region C: the same step with plain launches (one ctypes call per
-        # stage from Python, no graph), for comparison with region A
+        # the same graphs replayed reps_b times with an event between
+        # replays: the spread of the step time
+        step_ms = replay_times(torch, multi[0], reps_b) / G
+        del multi, single
+        # region B: per-stage device time, each stage's graph replayed
+        # reps_b times (independent of --steps)
+        per = time_stages(torch, chains, reps_b)
+        log(args, f"timed {reps_b} replays of {len(calls)} launches per stage")
+        # region C: plain launches (one ctypes call per stage, no graph)
         n_eager = min(args.steps, 500)
         for i in range(5):
             for f in calls[i % len(calls)]:
@@ -509,28 +662,16 @@ def main():
         eager_ms = (time.perf_counter() - te0) * 1e3 / n_eager
         log(args, f"timed {n_eager} plain-launch steps")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage_ms = np.zeros(len(names))
-    if args.eager:
-        for e in ev:
-            for j in range(len(names)):
-                stage_ms[j] += e[j].elapsed_time(e[j + 1])
-        stage_ms /= len(ev)
-    else:
-        for j, (a, b) in enumerate(ev):
-            stage_ms[j] = a.elapsed_time(b) / (reps * len(calls))
+    stages = stage_summary(per)
     steps_per_s = 1e3 / ms_per_step
 
     # algorithmic work
     logit_bytes = L * cfg.vocab * 4 + L * K * 8 + L * 4
-    flops = []
-    for dep in depths:
-        vis = P + (dep + 1)                       # prefix + ancestors incl. self
-        flops.append(4.0 * cfg.D * cfg.hq * float(vis.sum()))
-    verify_flops = float(np.mean(flops))
+    verify_flops = float(np.mean([ch.verify_flops for ch in chains]))
     drafter_bytes = ((ctx + L) * cfg.hkv * cfg.D * 2 * 2) + 2 * (L * cfg.hq * cfg.D * 2)
-    t_logit = stage_ms[1] * 1e-3
-    t_verify = stage_ms[3] * 1e-3
-    t_draft = stage_ms[0] * 1e-3
+    t_logit = stages["topk"]["mean"] * 1e-6
+    t_verify = stages["verify_attn"]["mean"] * 1e-6
+    t_draft = stages["drafter_attn"]["mean"] * 1e-6
     logit_gbs = logit_bytes / t_logit / 1e9
     verify_tflops = verify_flops / t_verify / 1e12
 
@@ -587,11 +728,14 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(verify_tflops / BF16_PEAK_TFLOPS, 5),
             "traffic": traffic,
+            "launch_us": stages["verify_attn"],
+            "replays": reps_b,
             "algorithmic_flops_per_launch": verify_flops,
             "issued_mfma_flops_per_launch": issued_mfma,
             "mfma_busy_pct_main_kernel": mfma_busy,
         },
-        "stages_us": {n: round(float(m) * 1e3, 3) for n, m in zip(names, stage_ms)},
+        "stages_us": {n: stages[n]["mean"] for n in names},
+        "stages_us_spread": stages,
         "logit_pass": {
             "bound": "hbm", "achieved": round(logit_gbs, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(logit_gbs / HBM_PEAK_GBS, 4),
@@ -606,11 +750,34 @@ def main():
     }
 
     if not args.eager:
+        mean, med, mn = spread(step_ms)
+        result["step_us_spread"] = {"mean": round(mean, 3), "median": round(med, 3),
+                                    "min": round(mn, 3), "replays": reps_b}
         result["plain_launches"] = {"steps": n_eager, "ms_per_step": round(eager_ms, 5),
                                     "steps_per_s": round(1e3 / eager_ms, 2)}
-    result["accept_36_layers"] = accept_layers_leg(torch, ddt, synth, steps, cases, cfg, dev)
-    result["tree_rope_kv"] = tree_rope_leg(torch, ddt, steps, cfg, dev)
-    result["packed_blocks_attn"] = packed_blocks_leg(torch, ddt, steps, cfg, dev)
+        fl = floor_leg(torch, ddt, dev, reps_b)
+        two = fl["one_launch_read_us"] + fl["dependent_launch_us"]
+        fl["two_launch_floor_us"] = round(two, 3)
+        fl["logit_pass_us"] = stages["topk"]["mean"]
+        fl["logit_pass_frac_of_floor"] = round(two / stages["topk"]["mean"], 4)
+        result["logit_pass"]["floor"] = fl
+    result["accept_36_layers"] = accept_layers_leg(torch, ddt, synth, chains, cases, cfg, dev)
+    result["tree_rope_kv"] = tree_rope_leg(torch, ddt, chains, cfg, dev)
+    result["packed_blocks_attn"] = packed_blocks_leg(torch, ddt, chains, cfg, dev)
+    if not args.no_workloads and not args.eager:
+        del calls
+        result["workloads"] = {
+            "c4_peaked": workload_leg(args, torch, ddt, synth, synth.CONFIGS[4], 4,
+                                      args.seed + 40, dev,
+                                      "ddtree_b1024_peaked: L=16 K=64 B=1024 P=4096", reps_b),
+            "c4_flat": workload_leg(args, torch, ddt, synth, synth.FLAT4, 4, args.seed + 41,
+                                    dev, "ddtree_b1024_flat: L=16 K=64 B=1024 P=4096, delta/2",
+                                    reps_b),
+            "c5_serving": workload_leg(args, torch, ddt, synth, synth.CONFIGS[5], 2,
+                                       args.seed + 50, dev,
+                                       "serving_b32: 32 requests x (L=16 K=16 B=64), "
+                                       "P~U{512..8192}, hq=32 hkv=4", max(10, reps_b // 5)),
+        }
     if not args.no_streams:
         result["verify_attn_serving"] = serving_verify_leg(args, torch, ddt, synth, dev)
     if not args.no_streams:
@@ -621,20 +788,35 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(case, budget_s, args):
-    """The oracle, as it stands, running the same chain step on the host."""
+    """The oracle, as it stands, running the same chain step on the host:
+    first with every core its numerical libraries use, then limited to one
+    thread; per-stage times in both modes.  About budget_s seconds of host
+    time per mode (at least one step each)."""
     import synth
     from oracle.accept import accept_compact
     from oracle.attention import masked_attention
     from oracle.logits import topk_logprobs
     from oracle.tree import build_trees
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl is in the image
+        threadpool_info = threadpool_limits = None
+        threads = 1
     cfg = case.cfg
-    L, N, ctx = cfg.L, cfg.B + 1, cfg.drafter_ctx
+    L, ctx = cfg.L, cfg.drafter_ctx
     dq = synth.bf16_bits_to_f32(case.dq_bits)
     dk = synth.bf16_bits_to_f32(case.dk_bits)
     dv = synth.bf16_bits_to_f32(case.dv_bits)
@@ -642,26 +824,58 @@ def cpu_baseline(case, budget_s, args):
     vk = synth.bf16_bits_to_f32(case.vk_bits)
     vv = synth.bf16_bits_to_f32(case.vv_bits)
     y = synth.sample_target_path(case)
-    n_steps = 0
-    t0 = time.perf_counter()
-    while True:
+    names = ["drafter_attn", "topk", "tree", "verify_attn", "accept"]
+
+    def one_step(acc):
+        t = [time.perf_counter()]
         masked_attention(dq, dk, dv, [0], [ctx], [L], None)
+        t.append(time.perf_counter())
         ids, logp, _ = topk_logprobs(case.logits, cfg.K)
-        t = build_trees(logp, ids, case.root_token, 1, L, cfg.k_tree, cfg.B)
-        masked_attention(vq, vk, vv, case.kv_base, case.prefix_len, t["n_nodes"], t["mask"])
-        tgt = synth.target_for_tree(t["token"][0], t["parent"][0], t["depth"][0],
-                                    int(t["n_nodes"][0]), y[0], case.off_path[0])[None]
-        accept_compact(t["token"], t["parent"], t["n_nodes"], tgt, L, case.vk_bits[None],
+        t.append(time.perf_counter())
+        tr = build_trees(logp, ids, case.root_token, 1, L, cfg.k_tree, cfg.B)
+        t.append(time.perf_counter())
+        masked_attention(vq, vk, vv, case.kv_base, case.prefix_len, tr["n_nodes"], tr["mask"])
+        t.append(time.perf_counter())
+        tgt = synth.target_for_tree(tr["token"][0], tr["parent"][0], tr["depth"][0],
+                                    int(tr["n_nodes"][0]), y[0], case.off_path[0])[None]
+        t0 = time.perf_counter()
+        accept_compact(tr["token"], tr["parent"], tr["n_nodes"], tgt, L, case.vk_bits[None],
                        case.vv_bits[None], case.kv_base, case.prefix_len)
-        n_steps += 1
-        el = time.perf_counter() - t0
-        log(args, f"cpu baseline step {n_steps}: {el:.1f}s")
-        if el >= budget_s:
-            break
-    return {"value": round(n_steps / el, 4), "unit": "steps/s", "cores": int(cores),
+        t.append(time.perf_counter() - (t0 - t[-1]))     # target drawing excluded
+        for j in range(len(names)):
+            acc[j] += t[j + 1] - t[j]
+
+    def run(mode):
+        acc = np.zeros(len(names))
+        n, t0 = 0, time.perf_counter()
+        while True:
+            one_step(acc)
+            n += 1
+            el = time.perf_counter() - t0
+            log(args, f"cpu baseline ({mode}) step {n}: {el:.1f}s")
+            if el >= budget_s:
+                break
+        return n, float(acc.sum()), {nm: round(a / n * 1e3, 2) for nm, a in zip(names, acc)}
+
+    n_all, t_all, st_all = run("all cores")
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            n_one, t_one, st_one = run("one thread")
+    else:
+        n_one, t_one, st_one = run("one thread")
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = os.cpu_count()
+    return {"value": round(n_all / t_all, 4), "unit": "steps/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{n_steps} full oracle chain steps on input set 0 ({el:.1f} s of host "
-                      f"time; float64 numpy, BLAS threads={cores})"}
+            "sample": f"{n_all} full oracle chain steps on input set 0 of the same workload "
+                      f"({t_all:.1f} s of host time; float64 numpy, numerical-library threads="
+                      f"{threads})",
+            "stage_ms": st_all,
+            "single_thread": {"value": round(n_one / t_one, 4), "unit": "steps/s", "cores": 1,
+                              "steps": n_one, "stage_ms": st_one},
+            "nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": _cpu_model()}
 
 
 if __name__ == "__main__":
