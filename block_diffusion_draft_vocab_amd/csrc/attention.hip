@@ -63,6 +63,7 @@ constexpr float kRescaleLog2 = 8.0f;
 constexpr int kMaxTilesPerSplit = 16;
 constexpr int kMinTilesPerSplit = 3;  // measured: 2 and 4 were slower for one 256-column group
 constexpr int kCUs = 256;
+constexpr int kXcds = 8;  // accelerator dies; consecutive workgroups go to different ones
 
 template <int D>
 struct Geo {
@@ -273,18 +274,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int h2 = lane >> 5;
   const int n = lane & 31;
 
-  // ---- decode the work item: (split, column group, request, KV head), KV
-  // head fastest.  The trailing partial group sits next to the full groups
-  // of the same split, so it runs while they do and finds the same K/V tiles
-  // in its XCD's L2; a group with fewer splits than the slot has exits.
-  int x = blockIdx.x;
+  // ---- decode the work item.  Workgroups are dealt round-robin to the 8
+  // XCDs (blockIdx % 8), each XCD starting its share in blockIdx order.
+  // The column groups of one (KV head, request, split) read the same K/V
+  // tiles, so they are made consecutive in one XCD's dispatch order: they
+  // run side by side and each tile comes from HBM once into that XCD's L2.
+  // The (KV head, request, split) triples themselves go round-robin over
+  // the XCDs, KV head fastest (one head per XCD for a single request with
+  // 8 KV heads; ragged requests spread evenly).
   const int n_groups = p.n_cg_full + (p.n_split_tail > 0 ? 1 : 0);
+  const int xcd = blockIdx.x % kXcds;
+  const int jx = blockIdx.x / kXcds;
+  const int cg = jx % n_groups;
+  int x = (jx / n_groups) * kXcds + xcd;
   const int hk = x % p.hkv;
   x /= p.hkv;
   const int r = x % p.batch;
-  x /= p.batch;
-  const int cg = x % n_groups;
-  const int s = x / n_groups;
+  const int s = x / p.batch;
+  if (s >= p.n_split && s >= p.n_split_tail) return;  // padding of the last round
   int n_split = cg < p.n_cg_full ? p.n_split : p.n_split_tail;
 
   // the request's sizes and cache base: three loads, one round trip
@@ -723,7 +730,9 @@ template <int D>
 hipError_t launch_d(const Params& prm, const AttnPlan& plan, hipStream_t stream) {
   const int n_groups = plan.n_cg_full + (plan.n_split_tail > 0 ? 1 : 0);
   const int max_split = plan.n_split > plan.n_split_tail ? plan.n_split : plan.n_split_tail;
-  const int wgs = n_groups * max_split * prm.batch * prm.hkv;
+  // (head, request, split) triples in rounds of kXcds, times the column groups
+  const long triples = (long)max_split * prm.batch * prm.hkv;
+  const int wgs = (int)(((triples + kXcds - 1) / kXcds) * kXcds * n_groups);
   constexpr size_t smem = Geo<D>::kSmem;
   if (wgs <= 0) return hipSuccess;
   if (plan_splits(plan)) {
