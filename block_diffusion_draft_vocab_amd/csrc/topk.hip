@@ -399,17 +399,19 @@ constexpr int kWaveCandCap = 512;  // keys >= T a wave ranks in LDS
 
 // The same merge with one wave per row and no block barrier, for rows whose
 // n = n_chunks * k keys fit R per lane (n <= 64 R) and whose threshold
-// candidates fit one per lane (n_chunks * ceil(k / n_chunks) <= 64).  Each
+// candidates fit C per lane (n_chunks * ceil(k / n_chunks) <= 64 C).  Each
 // lane holds R keys of the row in registers; the threshold T is
 // ranked among the candidates through a small LDS area of the wave; a wave
 // scan of the per-lane counts of keys >= T places those keys in LDS, and
-// each is ranked by counting the greater ones.
-template <int R>
+// each is ranked by counting the greater ones.  C = 2 serves rows where one
+// candidate per lane would leave no more candidates than k (T would be the
+// smallest list head and let most keys through).
+template <int R, int C>
 __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
     const uint64_t* __restrict__ part_key, const float2* __restrict__ part_ms, int n_rows,
     int n_chunks, int k, int32_t* __restrict__ ids, float* __restrict__ logp,
     float* __restrict__ lse_out) {
-  __shared__ alignas(16) uint64_t cand_all[kWaves][kWave];
+  __shared__ alignas(16) uint64_t cand_all[kWaves][kWave * C];
   __shared__ alignas(16) uint64_t take_all[kWaves][kWaveCandCap];
   const int wid = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -417,11 +419,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
   if (row >= n_rows) return;
   const int n = n_chunks * k;
   const uint64_t* lists = part_key + (int64_t)row * n;
-  // candidates: the first mm keys of every list, as many as fit one per
+  // candidates: the first mm keys of every list, as many as fit C per
   // lane (a larger set gives a tighter T and fewer keys to rank), at least
   // ceil(k / n_chunks) so that at least k candidates exist
-  const int mm = max((k + n_chunks - 1) / n_chunks, min(k, kWave / n_chunks));
-  const int ns = n_chunks * mm;  // <= 64 (host check)
+  const int mm = max((k + n_chunks - 1) / n_chunks, min(k, C * kWave / n_chunks));
+  const int ns = n_chunks * mm;  // <= 64 C (host check)
 
   // all global loads first: keys, threshold candidates, chunk (max, sum)
   // key r of this lane is key kidx(r) of the row: pairs of keys at 16-byte
@@ -444,7 +446,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) key[r] = lists[kidx(r) < n ? kidx(r) : 0];
   }
-  const uint64_t c = lists[lane < ns ? (lane / mm) * k + lane % mm : 0];
+  uint64_t c[C];
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    const int ci = lane + q * kWave;
+    c[q] = lists[ci < ns ? (ci / mm) * k + ci % mm : 0];
+  }
   const float2* ms = part_ms + (int64_t)row * n_chunks;
   const float2 p0 = ms[lane < n_chunks ? lane : 0];
   const float2 p1 = ms[lane + kWave < n_chunks ? lane + kWave : 0];
@@ -466,16 +473,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
   // T = k-th largest candidate (0 -- take every key -- when that rank is
   // only held by tied zero padding keys)
   uint64_t* cw = cand_all[wid];
-  const uint64_t cv = lane < ns ? c : 0ull;
-  cw[lane] = cv;
+  uint64_t cv[C];
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    cv[q] = lane + q * kWave < ns ? c[q] : 0ull;
+    cw[lane + q * kWave] = cv[q];
+  }
   wave_lds_sync();
-  const int crank = rank_among(cw, ns, cv);
-  const uint64_t hit = __ballot(lane < ns && crank == k - 1);
   uint64_t T = 0;
-  if (hit != 0) {
-    const int src = __builtin_ctzll(hit);
-    T = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cv >> 32), src) << 32) |
-        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cv, src);
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    const int crank = rank_among(cw, ns, cv[q]);
+    const uint64_t hit = __ballot(lane + q * kWave < ns && crank == k - 1);
+    if (hit != 0) {
+      const int src = __builtin_ctzll(hit);
+      T = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cv[q] >> 32), src)
+           << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cv[q], src);
+    }
   }
 
   // this lane's keys >= T
@@ -621,19 +636,30 @@ hipError_t launch_topk_merge(const uint64_t* part_key, const float2* part_ms, in
                              int n_chunks, int k, int32_t* ids, float* logp, float* lse,
                              hipStream_t stream) {
   const int n = n_chunks * k;
-  const int ns = n_chunks * ((k + n_chunks - 1) / n_chunks);
-  if (n <= 64 * 32 && ns <= kWave && n_chunks <= 2 * kWave) {
+  const int ns_min = n_chunks * ((k + n_chunks - 1) / n_chunks);
+  // candidates with one per lane; two per lane when that set would hold no
+  // more than k keys
+  const int ns1 = n_chunks * max((k + n_chunks - 1) / n_chunks, min(k, kWave / n_chunks));
+  const int cand = ns1 <= k && ns_min <= 2 * kWave && n_chunks * min(k, 2 * kWave / n_chunks) > ns1
+                       ? 2 : 1;
+  if (n <= 64 * 32 && ns_min <= cand * kWave && n_chunks <= 2 * kWave) {
     // one wave per workgroup for a few rows (each row's merge on its own
     // CU), four for many
     const int wpb = n_rows <= 64 ? 1 : kWaves;
     const dim3 grid((n_rows + wpb - 1) / wpb);
-#define DDT_MERGE_WAVE(RR)                                                                    \
-  hipLaunchKernelGGL(topk_merge_wave_kernel<RR>, grid, dim3(wpb * kWave), 0, stream, part_key, \
-                     part_ms, n_rows, n_chunks, k, ids, logp, lse)
-    if (n <= 64 * 4) DDT_MERGE_WAVE(4);
-    else if (n <= 64 * 8) DDT_MERGE_WAVE(8);
-    else if (n <= 64 * 16) DDT_MERGE_WAVE(16);
-    else DDT_MERGE_WAVE(32);
+#define DDT_MERGE_WAVE(RR, CC)                                                        \
+  hipLaunchKernelGGL((topk_merge_wave_kernel<RR, CC>), grid, dim3(wpb * kWave), 0, stream, \
+                     part_key, part_ms, n_rows, n_chunks, k, ids, logp, lse)
+    if (cand == 1) {
+      if (n <= 64 * 4) DDT_MERGE_WAVE(4, 1);
+      else if (n <= 64 * 8) DDT_MERGE_WAVE(8, 1);
+      else if (n <= 64 * 16) DDT_MERGE_WAVE(16, 1);
+      else DDT_MERGE_WAVE(32, 1);
+    } else {
+      if (n <= 64 * 8) DDT_MERGE_WAVE(8, 2);
+      else if (n <= 64 * 16) DDT_MERGE_WAVE(16, 2);
+      else DDT_MERGE_WAVE(32, 2);
+    }
 #undef DDT_MERGE_WAVE
     return hipGetLastError();
   }
