@@ -16,6 +16,11 @@ FAKE = ctypes.c_void_p(256)      # non-null, 16-byte aligned, never dereferenced
 
 @pytest.fixture(scope="module")
 def lib():
+    # DDT_ABI_TEST_LIB: the same library built with host sanitizers
+    # (tests/sanitize/build_sanitized.py; see test_abi_sanitized.py)
+    alt = os.environ.get("DDT_ABI_TEST_LIB")
+    if alt:
+        ddt._LIB_PATH = alt
     if not os.path.exists(ddt.lib_path()):
         pytest.fail("libddt.so is not built (python -m block_diffusion_draft_vocab_amd.build)")
     return ddt.load()
