@@ -43,7 +43,7 @@ constexpr int kLmCandCap = 256;  // keys >= T ranked per row in LDS
 constexpr float kLog2eLm = 1.4426950408889634f;
 
 __device__ __forceinline__ uint64_t lm_key(float x, int id) {
-  return ((uint64_t)f32_order(x) << 32) | (uint64_t)(~(uint32_t)id);
+  return ((uint64_t)f32_order(x + 0.0f) << 32) | (uint64_t)(~(uint32_t)id);  // -0 ties +0
 }
 
 __device__ __forceinline__ bf16x8 lds_b128_lm(uint32_t a) {

@@ -41,8 +41,10 @@ constexpr int kMergeMaxKeys = kTopkMergeMaxKeys;    // 16384: staged in LDS by t
 constexpr int kTopkPlanMaxLists = 128;  // chunk lists the logit pass itself plans
 constexpr float kLog2e = 1.4426950408889634f;
 
+// x + 0 turns -0 into +0 (and leaves every other value alone): the two
+// zeros are the same logit and tie, so the smaller id must win.
 __device__ __forceinline__ uint64_t make_key(float x, int id) {
-  return ((uint64_t)f32_order(x) << 32) | (uint64_t)(~(uint32_t)id);
+  return ((uint64_t)f32_order(x + 0.0f) << 32) | (uint64_t)(~(uint32_t)id);
 }
 
 // Rank of key v among cand[0..n) (number of greater keys), reading the

@@ -131,13 +131,14 @@ __global__ __launch_bounds__(1024) void tree_kernel(
   uint64_t* gb = keys;
   uint64_t* obuf = kbuf;
   int g = min(k_tree, B);
-  for (int i = tid; i < g; i += nt) gb[i] = tkey(y[i], 1, 0, i);
+  // a depth-1 score is the root's (0) plus the log-prob: -0 becomes +0
+  for (int i = tid; i < g; i += nt) gb[i] = tkey(0.0f + y[i], 1, 0, i);
   __syncthreads();
   uint64_t theta = (g == B && B > 0) ? gb[B - 1] : 0ull;
   const int nwaves = nt / kWave;
   // score of the best depth-(d-1) node: the rank-0 child of the previous
   // level's first parent (depth 1: rank 0 of row 0)
-  float best_prev = y[0];
+  float best_prev = 0.0f + y[0];
 
   for (int d = 2; d <= L && g > 0; ++d) {
     // The level's best possible child is the rank-0 child of its first

@@ -110,3 +110,16 @@ def test_topk_deterministic(gpu):
     b = _run(gpu, case.logits, 32)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_topk_signed_zero_ties(gpu):
+    """-0 and +0 are the same logit: they tie, and the smaller id ranks
+    first whichever sign it carries (vocab 4, and a row long enough to span
+    several chunks with zeros of both signs around the top)."""
+    small = np.array([[0.0, -0.0, 2.0, 0.0]], np.float32)
+    _compare(gpu, small, 4)
+    rng = np.random.default_rng(21)
+    big = np.round(rng.normal(0, 0.3, size=(3, 20000))).astype(np.float32) - 2.0
+    big[:, ::7] = 0.0
+    big[:, 3::7] = -0.0
+    _compare(gpu, big, 64)

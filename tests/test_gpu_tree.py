@@ -125,3 +125,15 @@ def test_tree_chained_from_gpu_topk(gpu):
         for path in set(gp) ^ set(op):
             sc = op.get(path, gp.get(path))
             assert abs(sc - boundary) <= 1e-5
+
+
+def test_tree_negative_zero_logprobs(gpu):
+    """A log-prob of -0.0 is a probability of 1: a node's score is its
+    parent's score plus the log-prob, so -0 becomes +0 and ties the other
+    zeros, broken by rank (scores compared bit for bit)."""
+    logp = np.array([[-0.0, 0.0, -0.5, -1.0],
+                     [0.0, -0.0, -0.25, -2.0],
+                     [-0.0, -0.0, -0.0, -3.0]], np.float32)
+    ids = np.array([[4, 7, 1, 9], [3, 8, 2, 6], [5, 1, 7, 0]], np.int32)
+    for B in (1, 3, 8, 20):
+        _check(gpu, logp, ids, [11], 1, 3, 4, B)

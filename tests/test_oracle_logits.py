@@ -181,3 +181,13 @@ def test_argmax_rejects_nan():
     z[0, 2] = np.nan
     with pytest.raises(ValueError):
         argmax_rows(z)
+
+
+def test_signed_zeros_tie():
+    """-0.0 and +0.0 are equal logits: ranked by id, as a plain sort on
+    (-x, id) orders them."""
+    from oracle.logits import topk_logprobs
+    z = np.array([[0.0, -0.0, 2.0, 0.0, -0.0]], np.float32)
+    ids, _, _ = topk_logprobs(z, 5)
+    expect = sorted(range(5), key=lambda i: (-float(z[0, i]), i))
+    assert ids[0].tolist() == expect == [2, 0, 1, 3, 4]
