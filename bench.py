@@ -81,10 +81,12 @@ def calibrate_copy(mib: int) -> None:
                       "bytes_written_per_launch": n * 4}))
 
 
-def time_graph(torch, fns, reps):
-    """Average device time of one call: a HIP graph holds every call of fns
-    back to back and is replayed reps times between HIP events recorded on
-    the launch stream."""
+def time_graph(torch, fns, reps, min_calls=20):
+    """Average device time of one call: a HIP graph holds the calls of fns
+    back to back, repeated until it holds at least min_calls calls (so the
+    graph's own launch cost is spread thin), and is replayed reps times
+    between HIP events recorded on the launch stream."""
+    fns = list(fns) * max(1, -(-min_calls // len(fns)))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -479,15 +481,19 @@ def make_chains(args, torch, ddt, synth, cfg, n_sets, seed0, dev):
     return cases, chains
 
 
-def time_stages(torch, chains, reps):
-    """Per-stage device time: one graph per stage holds that stage for every
-    input set back to back and is replayed reps times, a HIP event between
-    replays.  Returns {stage: per-launch ms of each replay}."""
+def time_stages(torch, chains, reps, min_launches=20):
+    """Per-stage device time: one graph per stage holds that stage for the
+    input sets back to back, cycling through them until the graph holds at
+    least min_launches launches (so the graph's own launch cost is spread
+    thin), and is replayed reps times, a HIP event between replays.
+    Returns {stage: per-launch ms of each replay}."""
     names = [n for n, _ in chains[0].stage_calls()]
+    cyc = max(1, -(-min_launches // len(chains)))
+    order = [ch for _ in range(cyc) for ch in chains]
     per = {}
     for j, name in enumerate(names):
-        g = capture(torch, [ch.stage_calls()[j][1] for ch in chains])
-        per[name] = replay_times(torch, g, reps) / len(chains)
+        g = capture(torch, [ch.stage_calls()[j][1] for ch in order])
+        per[name] = replay_times(torch, g, reps) / len(order)
         del g
     return per
 
@@ -507,10 +513,12 @@ def workload_leg(args, torch, ddt, synth, cfg, n_sets, seed0, dev, label, reps):
     bounds."""
     log(args, f"{label}: generating {n_sets} input sets")
     cases, chains = make_chains(args, torch, ddt, synth, cfg, n_sets, seed0, dev)
-    fns = [f for ch in chains for _, f in ch.stage_calls()]
+    # one graph of at least 8 steps, cycling through the input sets
+    cyc = max(1, -(-8 // n_sets))
+    fns = [f for _ in range(cyc) for ch in chains for _, f in ch.stage_calls()]
     warm_on_side_stream(torch, fns)
     g = capture(torch, fns)
-    step_ms = replay_times(torch, g, reps) / n_sets
+    step_ms = replay_times(torch, g, reps) / (n_sets * cyc)
     del g
     per = time_stages(torch, chains, reps)
     st = stage_summary(per)
