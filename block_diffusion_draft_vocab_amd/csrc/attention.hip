@@ -290,22 +290,35 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 
   // ---- decode the work item.  Workgroups are dealt round-robin to the 8
   // XCDs (blockIdx % 8), each XCD starting its share in blockIdx order.
-  // The column groups of one (KV head, request, split) read the same K/V
+  // The column groups of one (split, KV head, request) read the same K/V
   // tiles, so they are made consecutive in one XCD's dispatch order: they
   // run side by side and each tile comes from HBM once into that XCD's L2.
-  // The (KV head, request, split) triples themselves go round-robin over
-  // the XCDs, KV head fastest (one head per XCD for a single request with
-  // 8 KV heads; ragged requests spread evenly).
+  // The triples themselves go round-robin over the XCDs.  One request: KV
+  // head fastest, so with 8 KV heads each XCD holds one head and every
+  // split of a column group finds that group's Q rows in its L2 (measured:
+  // split fastest instead made the budget-256 verify launch 27 -> 39 us).
+  // Several requests: split fastest, so the splits of one request land on
+  // different XCDs and every XCD gets a similar mix of long and short
+  // requests (ragged serving batch 327 -> 303 us per step stage).
   const int n_groups = p.n_cg_full + (p.n_split_tail > 0 ? 1 : 0);
+  const int max_split = p.n_split > p.n_split_tail ? p.n_split : p.n_split_tail;
   const int xcd = blockIdx.x % kXcds;
   const int jx = blockIdx.x / kXcds;
   const int cg = jx % n_groups;
   int x = (jx / n_groups) * kXcds + xcd;
-  const int hk = x % p.hkv;
-  x /= p.hkv;
-  const int r = x % p.batch;
-  const int s = x / p.batch;
-  if (s >= p.n_split && s >= p.n_split_tail) return;  // padding of the last round
+  int s, hk, r;
+  if (p.batch == 1) {
+    hk = x % p.hkv;
+    r = 0;
+    s = x / p.hkv;
+    if (s >= max_split) return;  // padding of the last round
+  } else {
+    s = x % max_split;
+    x /= max_split;
+    hk = x % p.hkv;
+    r = x / p.hkv;
+    if (r >= p.batch) return;  // padding of the last round
+  }
   int n_split = cg < p.n_cg_full ? p.n_split : p.n_split_tail;
 
   // the request's sizes and cache base: three loads, one round trip
