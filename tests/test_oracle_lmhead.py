@@ -66,3 +66,16 @@ def test_planted_token_on_top_and_definition():
     # the logit-pass definition on the float32 logits
     ids2, logp2, lse2 = topk_logprobs(z64.astype(np.float32), 8)
     assert np.array_equal(ids, ids2) and np.array_equal(logp, logp2)
+
+
+def test_temperature_scales_integer_logit_gaps():
+    """Integer inputs give exact integer logits; at inv_temperature 1/2 the
+    scaled logits stay exact in float32, so the log-prob gaps are exactly
+    half the logit gaps and the full-vocabulary distribution sums to 1."""
+    hb, wb, _ = synth.make_lmhead_case(6, 3, 128, 64, integer=True)
+    z = lmhead_logits(hb, wb)
+    ids, logp, _, _ = lmhead_topk(hb, wb, 64, inv_temperature=0.5)
+    for r in range(3):
+        gaps = logp[r].astype(np.float64) - logp[r, 0]
+        assert np.allclose(gaps, 0.5 * (z[r, ids[r]] - z[r, ids[r, 0]]), atol=2e-6)
+        assert abs(np.exp(logp[r].astype(np.float64)).sum() - 1.0) < 1e-5
