@@ -180,14 +180,49 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One ds_read_b64_tr_b16 (issued as inline asm: the compiler's intrinsic
-// makes every use wait for all LDS-direct copies in flight, including the
-// ones for later tiles).  The caller waits on lgkmcnt with lds_wait_all.
-template <int OFF>
-__device__ __forceinline__ i16x4 lds_tr(uint32_t addr) {
-  i16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-  return r;
+// The V^T fragments of one 16-key chunk: 2R ds_read_b64_tr_b16 and their
+// wait, in one asm statement.  (The compiler's intrinsic makes every use wait
+// for all LDS-direct copies in flight, including the ones for later tiles;
+// in inline asm a read left in flight past its statement could land in a
+// register the compiler has already reused, so each statement waits for its
+// own reads.)  Fragment dt reads columns 32 dt of rows R0 / R1 from base
+// va0 (even dt) or va1 (odd dt), the second pair of fragments 128 bytes on.
+// Outputs are early-clobber: no read may overwrite an address register
+// before a later read of the statement has used it.
+template <int R, int R0, int R1>
+__device__ __forceinline__ void lds_tr_chunk(uint32_t va0, uint32_t va1, i16x4 (&t)[R][2]) {
+  if constexpr (R == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%10\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1]), "=&v"(t[2][0]),
+          "=&v"(t[2][1]), "=&v"(t[3][0]), "=&v"(t[3][1])
+        : "v"(va0), "v"(va1), "i"(R0), "i"(R1), "i"(R0 + 128), "i"(R1 + 128));
+  } else if constexpr (R == 2) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1])
+        : "v"(va0), "v"(va1), "i"(R0), "i"(R1));
+  } else {
+    static_assert(R == 1, "head_dim");
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
+        "ds_read_b64_tr_b16 %1, %2 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0][0]), "=&v"(t[0][1])
+        : "v"(va0), "i"(R0), "i"(R1));
+  }
 }
 __device__ __forceinline__ bf16x8 join(i16x4 lo, i16x4 hi) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -206,40 +241,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (I < N) {
     f(IntC<I>{});
     static_for<N, I + 1>(f);
-  }
-}
-
-// Wait for every LDS read in flight; the registers of t are tied to the
-// wait so that no use of them can be scheduled above it.
-template <int R>
-__device__ __forceinline__ void lds_wait_all(i16x4 (&t)[R][2]) {
-  if constexpr (R == 1) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(t[0][0]), "+v"(t[0][1]));
-  } else if constexpr (R == 2) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]));
-  } else {
-    static_assert(R == 4, "head_dim");
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]), "+v"(t[2][0]),
-                   "+v"(t[2][1]), "+v"(t[3][0]), "+v"(t[3][1]));
-  }
-}
-
-// Wait until only the newest 2R LDS reads (the next chunk's) are in flight;
-// the registers of t (the older chunk) are tied to the wait.
-template <int R>
-__device__ __forceinline__ void lds_wait_keep(i16x4 (&t)[R][2]) {
-  if constexpr (R == 1) {
-    asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(t[0][0]), "+v"(t[0][1]));
-  } else if constexpr (R == 2) {
-    asm volatile("s_waitcnt lgkmcnt(4)"
-                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]));
-  } else {
-    static_assert(R == 4, "head_dim");
-    asm volatile("s_waitcnt lgkmcnt(8)"
-                 : "+v"(t[0][0]), "+v"(t[0][1]), "+v"(t[1][0]), "+v"(t[1][1]), "+v"(t[2][0]),
-                   "+v"(t[2][1]), "+v"(t[3][0]), "+v"(t[3][1]));
   }
 }
 
@@ -397,15 +398,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   // list is built.  Prefix tiles are always processed; a range that starts
   // in the own rows is copied speculatively and re-copied below in the rare
   // case that the list skips one of those tiles.
-  // (the Q loads are inline asm: the compiler cannot tell them apart from
-  // the tile copies issued after them and would wait for all of them)
   bf16x8 qf[D / 16];
   {
-    const uint16_t* qp = p.q + (((int64_t)r * p.n_q_max + qi) * p.hq + head) * D + 8 * h2;
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+        p.q + (((int64_t)r * p.n_q_max + qi) * p.hq + head) * D + 8 * h2);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(qf[t]) : "v"(qp + 16 * t));
+    for (int t = 0; t < D / 16; ++t) qf[t] = qp[2 * t];
   }
+  __builtin_amdgcn_sched_barrier(0);  // the Q loads stay ahead of the tile copies
   const int n_spec = min(2, t_end - t_begin);
   issue_tile(t_begin, 0);
   if (n_spec > 1) issue_tile(t_begin + 1, 1);
@@ -488,9 +488,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 
   // prologue: if the list does not start with the speculated tiles, let
   // those copies land and copy the right ones.  Then Q and tile 0 are
-  // waited for (tile 1 may stay in flight: inside the loop the only memory
-  // operations in flight are tile copies, so "all but the newest tile" is a
-  // plain vmcnt).
+  // waited for.  (The compiler, which cannot order the Q loads against the
+  // LDS-direct copies, waits for every copy before the first use of Q, so
+  // tile 1 has landed too; inside the loop the only memory operations in
+  // flight are tile copies, so "all but the newest tile" is a plain vmcnt.)
   if ((ntl > 0 && tile_at(0) != t_begin) || (ntl > 1 && n_spec > 1 && tile_at(1) != t_begin + 1) ||
       (ntl > 1 && n_spec < 2)) {
     wait_vm<0>();
@@ -504,10 +505,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   // Q was issued before every tile copy, so it has landed; columns past the
   // end (loaded from row 0 of the request) are zeroed
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    asm volatile("" : "+v"(qf[t]));
+  for (int t = 0; t < D / 16; ++t)
     if (!valid) qf[t] = bf16x8{};
-  }
 
   for (int i = 0; i < ntl; ++i) {
     // this tile's copies done (the next tile's may stay in flight), then
@@ -598,32 +597,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     }
     l_run += ls;
     const uint32_t va0 = vb + voff[0], va1 = vb + voff[1];
-    // V^T fragments of key chunk c (tile rows [16c, 16c+16)); chunk c+1's
-    // reads are issued before chunk c's MFMAs
-    auto read_chunk = [&](auto cc, i16x4 (&t)[D / 32][2]) {
-      constexpr int c = decltype(cc)::value;
-      constexpr int r0 = 16 * c * G::kRowBytes, r1 = r0 + 8 * G::kRowBytes;
-      static_for<D / 32>([&](auto dd) {
-        constexpr int dt = decltype(dd)::value;
-        const uint32_t va = (dt & 1) ? va1 : va0;
-        t[dt][0] = lds_tr<r0 + (dt >> 1) * 128>(va);
-        t[dt][1] = lds_tr<r1 + (dt >> 1) * 128>(va);
-      });
-    };
-    i16x4 tv[2][D / 32][2];
-    read_chunk(IntC<0>{}, tv[0]);
+    // V^T fragments of key chunk c (tile rows [16c, 16c+16)), then its
+    // MFMAs; those run while the next chunk's reads are waited for
     static_for<4>([&](auto cc) {
       constexpr int c = decltype(cc)::value;
-      if constexpr (c < 3) {
-        read_chunk(IntC<c + 1>{}, tv[(c + 1) & 1]);
-        lds_wait_keep<D / 32>(tv[c & 1]);
-      } else {
-        lds_wait_all(tv[c & 1]);
-      }
+      constexpr int r0 = 16 * c * G::kRowBytes, r1 = r0 + 8 * G::kRowBytes;
+      i16x4 tv[D / 32][2];
+      lds_tr_chunk<D / 32, r0, r1>(va0, va1, tv);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(tv[c & 1][dt][0], tv[c & 1][dt][1]),
-                                                        pf[c], o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(join(tv[dt][0], tv[dt][1]), pf[c], o[dt],
+                                                        0, 0, 0);
     });
   }
   // ---- result rows (bf16): the output itself without splits, else this
