@@ -125,14 +125,14 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     const int rk = i - d * k_tree;
     y[i] = logp[((int64_t)r * L + d) * K + rk];
   }
-  __syncthreads();
   // gb: G (sorted, g keys) with the level's children appended after it;
   // obuf: the other buffer of the merge ping-pong
   uint64_t* gb = keys;
   uint64_t* obuf = kbuf;
   int g = min(k_tree, B);
   // a depth-1 score is the root's (0) plus the log-prob: -0 becomes +0
-  for (int i = tid; i < g; i += nt) gb[i] = tkey(0.0f + y[i], 1, 0, i);
+  // (read from the input, so G and the table fill in the same pass)
+  for (int i = tid; i < g; i += nt) gb[i] = tkey(0.0f + logp[(int64_t)r * L * K + i], 1, 0, i);
   __syncthreads();
   uint64_t theta = (g == B && B > 0) ? gb[B - 1] : 0ull;
   const int nwaves = nt / kWave;
@@ -150,29 +150,35 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     const float best_child = best_prev + yd[0];
     if (g == B && !(tkey(best_child, d, 0, 0) > theta)) break;
     best_prev = best_child;
-    // parents: the depth d-1 members of G, numbered in G order (a ballot
-    // per 64-position chunk, then the chunk counts summed directly)
-    const int nchunk = (g + kWave - 1) / kWave;
-    for (int c = wid; c < nchunk; c += nwaves) {
-      const int q = c * kWave + lane;
-      const bool is = q < g && key_depth(gb[q]) == d - 1;
-      const uint64_t bal = __ballot(is);
-      if (lane == 0) wcnt[c] = __popcll(bal);
-      if (is) slot_tab[q] = __popcll(bal & lanemask_lt());
+    // parents: the depth d-1 members of G, numbered in G order.  At depth
+    // 2 that is all of G (only depth-1 nodes so far), parent j = G[j], whose
+    // score is 0 + y[j]; it is written with the run lengths below.
+    // Deeper: a ballot per 64-position chunk, then the chunk counts summed
+    // directly.
+    int n = g;
+    if (d > 2) {
+      const int nchunk = (g + kWave - 1) / kWave;
+      for (int c = wid; c < nchunk; c += nwaves) {
+        const int q = c * kWave + lane;
+        const bool is = q < g && key_depth(gb[q]) == d - 1;
+        const uint64_t bal = __ballot(is);
+        if (lane == 0) wcnt[c] = __popcll(bal);
+        if (is) slot_tab[q] = __popcll(bal & lanemask_lt());
+      }
+      __syncthreads();
+      // inclusive prefix of the chunk counts across the lanes of every wave
+      // (nchunk <= 32); q / 64 is uniform across a wave in the loop below
+      const int cinc = wave_inclusive_scan(lane < nchunk ? wcnt[lane] : 0);
+      n = __builtin_amdgcn_readlane(cinc, kWave - 1);
+      if (n == 0) break;
+      for (int q = tid; q < g; q += nt) {
+        const int c = q / kWave;
+        const int pre = c > 0 ? __builtin_amdgcn_readlane(cinc, c - 1) : 0;
+        const uint64_t kq = gb[q];
+        if (key_depth(kq) == d - 1) pscore[pre + slot_tab[q]] = key_score(kq);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    // inclusive prefix of the chunk counts across the lanes of every wave
-    // (nchunk <= 32); q / 64 is uniform across a wave in the loop below
-    const int cinc = wave_inclusive_scan(lane < nchunk ? wcnt[lane] : 0);
-    const int n = __builtin_amdgcn_readlane(cinc, kWave - 1);
-    if (n == 0) break;
-    for (int q = tid; q < g; q += nt) {
-      const int c = q / kWave;
-      const int pre = c > 0 ? __builtin_amdgcn_readlane(cinc, c - 1) : 0;
-      const uint64_t kq = gb[q];
-      if (key_depth(kq) == d - 1) pscore[pre + slot_tab[q]] = key_score(kq);
-    }
-    __syncthreads();
     // run length of parent j: children (j, c) with key above theta and
     // (j+1)(c+1) <= B; keys fall with c, so a binary search finds it.
     // Thread t owns parents [t*per, t*per + per).
@@ -186,7 +192,13 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       int len = 0;
       if (u < per && j < n) {
         int lo = 0, hi = min(k_tree, B / (j + 1));
-        const float ps = pscore[j];
+        float ps;
+        if (d == 2) {
+          ps = 0.0f + y[j];  // the key of G[j], exactly
+          pscore[j] = ps;    // read by the children pass, after a barrier
+        } else {
+          ps = pscore[j];
+        }
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
           if (tkey(ps + yd[mid], d, j, mid) > theta) lo = mid + 1;
@@ -353,22 +365,47 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     if (score_out != nullptr) score_out[ob + s] = sc;
   }
   if (tid == 0) n_nodes_out[r] = g + 1;
+  // ancestor masks in two passes.  First every word of every row, word
+  // index fastest (whole rows stored in order), with the bits that need no
+  // walk: the root's and the row's own.  Then, after a barrier orders the
+  // stores, one thread per row walks up from its parent once and rewrites
+  // each word that holds an intermediate ancestor (parents precede
+  // children, so the walk visits words in non-increasing order and reaches
+  // the root in <= L steps).
+  const float inv_w = 1.0f / (float)W;
   for (int idx = tid; idx < n_max * W; idx += nt) {
-    const int s = idx / W;
+    int s = (int)((float)idx * inv_w);  // idx < 2^24: exact after the fix-up
+    if (s * W > idx) --s;
+    if ((s + 1) * W <= idx) ++s;
     const int w = idx - s * W;
     uint64_t word = 0;
     if (s <= g) {
-      // parents precede children, so the walk reaches the root in <= L steps
-      int a = s;
-      for (int step = 0; step <= L; ++step) {
-        if ((a >> 6) == w) word |= 1ull << (a & 63);
-        if (a <= 0) break;
-        const int pa = par_slot[a];
-        if (pa < 0 || pa >= a) break;
-        a = pa;
-      }
+      if (w == 0) word = 1ull;
+      if ((s >> 6) == w) word |= 1ull << (s & 63);
     }
     mask_out[ob * W + idx] = word;
+  }
+  __syncthreads();
+  for (int s = 1 + tid; s <= g; s += nt) {
+    uint64_t* mrow = mask_out + (ob + s) * W;
+    const int sw = s >> 6;
+    const uint64_t sbit = 1ull << (s & 63);
+    int a = par_slot[s];
+    int cw = -1;
+    uint64_t acc = 0;
+    for (int step = 0; step < L && a > 0 && a < s; ++step) {
+      const int wa = a >> 6;
+      if (wa != cw) {
+        if (cw >= 0) mrow[cw] = acc | (cw == 0 ? 1ull : 0ull) | (cw == sw ? sbit : 0ull);
+        cw = wa;
+        acc = 0;
+      }
+      acc |= 1ull << (a & 63);
+      const int pa = par_slot[a];
+      if (pa >= a) break;
+      a = pa;
+    }
+    if (cw >= 0) mrow[cw] = acc | (cw == 0 ? 1ull : 0ull) | (cw == sw ? sbit : 0ull);
   }
 }
 
