@@ -85,6 +85,11 @@ size_t tree_smem_bytes(int L, int k_tree, int budget) {
 
 namespace {
 
+// Elements one thread carries through the register merge (levels with at
+// most one candidate per thread, or more than this many, take the
+// merge-path rounds).
+constexpr int kMaxCarry = 8;
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & (kWave - 1);
   return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
@@ -239,46 +244,133 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     for (int j = tid; j <= n + 1; j += nt)  // offsets of runs 0..n, and the end
       roff[j] = j == 0 ? 0 : (j <= n ? g + rcnt[j - 1] : g + nc);
     __syncthreads();
-    // pairwise merge-path rounds: runs (2i, 2i+1) -> run i, every output
-    // element placed independently by a binary search on its diagonal
     const int total = g + nc;
-    int R = n + 1;
-    uint64_t* src = gb;
-    uint64_t* dst = obuf;
-    int* ro = roff;
-    int* ro_next = roff2;
-    while (R > 1) {
-      const int Rn = (R + 1) >> 1;
-      for (int p = tid; p < total; p += nt) {
-        // pair i with ro[2i] <= p < ro[2i+2]
-        int lo = 0, hi = Rn - 1;
-        while (lo < hi) {
-          const int m = (lo + hi + 1) >> 1;
-          if (ro[2 * m] <= p) lo = m; else hi = m - 1;
+    if (total > nt && total <= kMaxCarry * nt) {
+      // Several elements per thread: pairwise rounds, runs (2i, 2i+1) ->
+      // run i, each element placed by its own thread.  Element e of
+      // [0, total) stays with thread e % nt (slot e / nt) for every round,
+      // its key in registers; its index in the merged run is its index in
+      // its own run plus the number of keys of the partner run above it
+      // (keys are distinct: depth, parent and rank are part of them), one
+      // binary search.  A merged run keeps its left run's start and at most
+      // B elements: an element with B or more keys above it in any subset
+      // cannot be in the top B, and neither can anything below it, so it
+      // drops out, and later rounds move fewer elements.
+      uint64_t xk[kMaxCarry];
+      int xrun[kMaxCarry], xidx[kMaxCarry];
+#pragma unroll
+      for (int m = 0; m < kMaxCarry; ++m) {
+        const int e = tid + m * nt;
+        xrun[m] = -1;
+        xidx[m] = 0;
+        xk[m] = 0ull;
+        if (e < total) {
+          const uint64_t x = gb[e];
+          xk[m] = x;
+          // G is run 0; a child's run (parent j + 1) and index (its rank)
+          // are in its key
+          const int pr = key_pr(x);
+          xrun[m] = e < g ? 0 : (pr >> 7) + 1;
+          xidx[m] = e < g ? e : (pr & 127);
         }
-        const int a0 = ro[2 * lo];
-        const int a1 = ro[2 * lo + 1];
-        const int b1 = 2 * lo + 2 <= R ? ro[2 * lo + 2] : a1;
-        const int la = a1 - a0, lb = b1 - a1;
-        const int kk = p - a0;
-        int l2 = kk - lb > 0 ? kk - lb : 0;
-        int h2 = kk < la ? kk : la;
-        while (l2 < h2) {
-          const int m = (l2 + h2) >> 1;
-          if (src[a0 + m] > src[a1 + kk - 1 - m]) l2 = m + 1; else h2 = m;
-        }
-        const int ai = l2, bi = kk - l2;
-        const bool take_a = bi >= lb || (ai < la && src[a0 + ai] > src[a1 + bi]);
-        dst[p] = take_a ? src[a0 + ai] : src[a1 + bi];
       }
-      for (int i = tid; i <= Rn; i += nt) ro_next[i] = i < Rn ? ro[2 * i] : total;
-      __syncthreads();
-      uint64_t* t = src; src = dst; dst = t;
-      int* u = ro; ro = ro_next; ro_next = u;
-      R = Rn;
+      // run lengths after the first round (which takes them from the
+      // offsets), in the parent-score / run-count / slot arrays (3 Bp ints,
+      // free until the next level): at most (B + 2) / 2, then half as many
+      // for the round after, ping-ponged
+      int* rl = nullptr;
+      int* rl_next = reinterpret_cast<int*>(pscore);
+      int* rl_spare = rl_next + (B + 2) / 2 + 1;
+      int R = n + 1;
+      uint64_t* src = gb;
+      uint64_t* dst = obuf;
+      int* rs = roff;
+      int* rs_next = roff2;
+      while (R > 1) {
+        const int Rn = (R + 1) >> 1;
+#pragma unroll
+        for (int m = 0; m < kMaxCarry; ++m) {
+          const int i = xrun[m];
+          if (i < 0) continue;
+          const int pi = i ^ 1;
+          int above = 0;
+          if (pi < R) {
+            const int b0 = rs[pi];
+            int lo = 0, hi = rl != nullptr ? rl[pi] : rs[pi + 1] - b0;
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (src[b0 + mid] > xk[m]) lo = mid + 1;
+              else hi = mid;
+            }
+            above = lo;
+          }
+          const int ni = xidx[m] + above;
+          if (ni >= B) {
+            xrun[m] = -1;
+          } else {
+            dst[rs[i & ~1] + ni] = xk[m];
+            xrun[m] = i >> 1;
+            xidx[m] = ni;
+          }
+        }
+        for (int k = tid; k < Rn; k += nt) {
+          rs_next[k] = rs[2 * k];
+          const int la = rl != nullptr ? rl[2 * k] : rs[2 * k + 1] - rs[2 * k];
+          const int lb = 2 * k + 1 >= R ? 0
+                         : (rl != nullptr ? rl[2 * k + 1] : rs[2 * k + 2] - rs[2 * k + 1]);
+          rl_next[k] = la + lb < B ? la + lb : B;
+        }
+        __syncthreads();
+        uint64_t* t = src; src = dst; dst = t;
+        int* u = rs; rs = rs_next; rs_next = u;
+        int* w = rl_next;
+        rl_next = rl != nullptr ? rl : rl_spare;
+        rl = w;
+        R = Rn;
+      }
+      gb = src;
+      obuf = dst;
+    } else {
+      // pairwise merge-path rounds: runs (2i, 2i+1) -> run i, every output
+      // element placed independently by a binary search on its diagonal
+      int R = n + 1;
+      uint64_t* src = gb;
+      uint64_t* dst = obuf;
+      int* ro = roff;
+      int* ro_next = roff2;
+      while (R > 1) {
+        const int Rn = (R + 1) >> 1;
+        for (int p = tid; p < total; p += nt) {
+          // pair i with ro[2i] <= p < ro[2i+2]
+          int lo = 0, hi = Rn - 1;
+          while (lo < hi) {
+            const int m = (lo + hi + 1) >> 1;
+            if (ro[2 * m] <= p) lo = m; else hi = m - 1;
+          }
+          const int a0 = ro[2 * lo];
+          const int a1 = ro[2 * lo + 1];
+          const int b1 = 2 * lo + 2 <= R ? ro[2 * lo + 2] : a1;
+          const int la = a1 - a0, lb = b1 - a1;
+          const int kk = p - a0;
+          int l2 = kk - lb > 0 ? kk - lb : 0;
+          int h2 = kk < la ? kk : la;
+          while (l2 < h2) {
+            const int m = (l2 + h2) >> 1;
+            if (src[a0 + m] > src[a1 + kk - 1 - m]) l2 = m + 1; else h2 = m;
+          }
+          const int ai = l2, bi = kk - l2;
+          const bool take_a = bi >= lb || (ai < la && src[a0 + ai] > src[a1 + bi]);
+          dst[p] = take_a ? src[a0 + ai] : src[a1 + bi];
+        }
+        for (int i = tid; i <= Rn; i += nt) ro_next[i] = i < Rn ? ro[2 * i] : total;
+        __syncthreads();
+        uint64_t* t = src; src = dst; dst = t;
+        int* u = ro; ro = ro_next; ro_next = u;
+        R = Rn;
+      }
+      gb = src;
+      obuf = dst;
     }
-    gb = src;
-    obuf = dst;
     g = min(B, total);
     theta = (g == B) ? gb[B - 1] : 0ull;
   }
