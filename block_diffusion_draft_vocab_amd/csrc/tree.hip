@@ -184,6 +184,72 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       }
       __syncthreads();
     }
+    // A level with many candidates per thread first narrows theta: a
+    // score s_lo with at least B candidates at or above it bounds the B-th
+    // key from below, so children below s_lo can be left out before the
+    // merge (the merge cut at B stays exact).  The candidates are G and the
+    // children (j, c) with c < min(k_tree, B / (j + 1)); each wave counts
+    // those at or above one probe score (parents spread over its lanes, G
+    // in 64 slices), and every round keeps the highest probe that still
+    // has B candidates, until at most B + B/4 remain above the bound.
+    {
+      int est_l = 0;
+      for (int j = lane; j < n; j += kWave) est_l += min(k_tree, B / (j + 1));
+      const int est = g + __builtin_amdgcn_readlane(wave_inclusive_scan(est_l), kWave - 1);
+      if (est > nt && est > 2 * B) {
+        auto ps_of = [&](int j) { return d == 2 ? 0.0f + y[j] : pscore[j]; };
+        // lowest candidate score: the last child of every parent, and G's last
+        float mn = key_score(gb[g - 1]);
+        for (int j = lane; j < n; j += kWave)
+          mn = fminf(mn, ps_of(j) + yd[min(k_tree, B / (j + 1)) - 1]);
+        float lo_f = -wave_max_f(-mn);
+        float hi_f = best_child;
+        int cnt_lo = est;
+        const int seg = (g + kWave - 1) / kWave;
+        for (int round = 0; round < 4 && cnt_lo > B + B / 4; ++round) {
+          const float t = lo_f + (hi_f - lo_f) * (float)(wid + 1) / (float)(nwaves + 1);
+          int c_l = 0;
+          for (int j = lane; j < n; j += kWave) {
+            const float ps = ps_of(j);
+            int lo = 0, hi = min(k_tree, B / (j + 1));
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (ps + yd[mid] >= t) lo = mid + 1;
+              else hi = mid;
+            }
+            c_l += lo;
+          }
+          {  // G slice [lane * seg, lane * seg + seg), scores non-increasing
+            int lo = lane * seg < g ? lane * seg : g;
+            int hi = lo + seg < g ? lo + seg : g;
+            const int b = lo;
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if (key_score(gb[mid]) >= t) lo = mid + 1;
+              else hi = mid;
+            }
+            c_l += lo - b;
+          }
+          const int cnt = __builtin_amdgcn_readlane(wave_inclusive_scan(c_l), kWave - 1);
+          if (lane == 0) wcnt[round * 64 + wid] = cnt;
+          __syncthreads();
+          int k = -1;
+          for (int w = 0; w < nwaves; ++w)
+            if (wcnt[round * 64 + w] >= B) k = w;
+          const float t_lo = k >= 0 ? lo_f + (hi_f - lo_f) * (float)(k + 1) / (float)(nwaves + 1)
+                                    : lo_f;
+          const float t_hi = k + 1 < nwaves
+                                 ? lo_f + (hi_f - lo_f) * (float)(k + 2) / (float)(nwaves + 1)
+                                 : hi_f;
+          if (k >= 0) cnt_lo = wcnt[round * 64 + k];
+          lo_f = t_lo;
+          hi_f = t_hi;
+        }
+        // children with a score >= lo_f have keys above this bound
+        const uint64_t bound = ((uint64_t)f32_order(0.0f + lo_f) << 32) - 1ull;
+        if (bound > theta) theta = bound;
+      }
+    }
     // run length of parent j: children (j, c) with key above theta and
     // (j+1)(c+1) <= B; keys fall with c, so a binary search finds it.
     // Thread t owns parents [t*per, t*per + per).
