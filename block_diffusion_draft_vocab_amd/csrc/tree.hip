@@ -95,6 +95,10 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 }
 
+// kPrune: levels with many candidates per thread narrow theta first (the
+// launch picks it from the depth-2 candidate bound; a kernel without that
+// code stays smaller, which the single-workgroup budget-256 tree notices).
+template <bool kPrune>
 __global__ __launch_bounds__(1024) void tree_kernel(
     const float* __restrict__ logp, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ root_token, int L, int K, int k_tree, int B, int cand_cap,
@@ -184,7 +188,8 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       }
       __syncthreads();
     }
-    // A level with many candidates per thread first narrows theta: a
+    // With kPrune, a level with many candidates per thread first narrows
+    // theta: a
     // score s_lo with at least B candidates at or above it bounds the B-th
     // key from below, so children below s_lo can be left out before the
     // merge (the merge cut at B stays exact).  The candidates are G and the
@@ -192,10 +197,15 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     // those at or above one probe score (parents spread over its lanes, G
     // in 64 slices), and every round keeps the highest probe that still
     // has B candidates, until at most B + B/4 remain above the bound.
-    {
-      int est_l = 0;
-      for (int j = lane; j < n; j += kWave) est_l += min(k_tree, B / (j + 1));
-      const int est = g + __builtin_amdgcn_readlane(wave_inclusive_scan(est_l), kWave - 1);
+    if constexpr (kPrune) {
+      // bound on the candidate count (no pass over the parents): the first
+      // m0 = min(n, B / k_tree) parents give k_tree children each, parent j
+      // beyond them at most B / (j + 1) <= B / (m0 + 1) + B ln(n / (m0 + 1)) in all
+      const int m0 = min(n, B / k_tree);
+      const float tail_ub = n > m0 ? (float)B / (float)(m0 + 1) +
+                                         (float)B * __logf((float)n / (float)(m0 + 1))
+                                   : 0.f;
+      const int est = g + m0 * k_tree + (int)tail_ub + 1;
       if (est > nt && est > 2 * B) {
         auto ps_of = [&](int j) { return d == 2 ? 0.0f + y[j] : pscore[j]; };
         // lowest candidate score: the last child of every parent, and G's last
@@ -577,12 +587,25 @@ hipError_t launch_tree(const float* logp, const int32_t* ids, const int32_t* roo
   // enough threads for one merge element per thread at the common sizes
   int threads = 256;
   while (threads < 1024 && threads < lay.cand_cap) threads <<= 1;
+  // depth 2 has the most candidates per parent: all min(k_tree, B) depth-1
+  // nodes are parents, parent j with at most min(k_tree, B / (j + 1))
+  // children
+  const int n2 = k_tree < budget ? k_tree : budget;
+  long cand2 = n2;
+  for (int j = 0; j < n2; ++j) cand2 += k_tree < budget / (j + 1) ? k_tree : budget / (j + 1);
+  const bool prune = L > 1 && cand2 > threads && cand2 > 2L * budget;
+  const void* fn = prune ? reinterpret_cast<const void*>(tree_kernel<true>)
+                         : reinterpret_cast<const void*>(tree_kernel<false>);
   if (lay.bytes > 64 * 1024)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(tree_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
-  hipLaunchKernelGGL(tree_kernel, dim3(batch), dim3(threads), lay.bytes, stream, logp, ids,
-                     root, L, k, k_tree, budget, lay.cand_cap, n_nodes, token, parent, depth,
-                     score, mask);
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
+  if (prune)
+    hipLaunchKernelGGL(tree_kernel<true>, dim3(batch), dim3(threads), lay.bytes, stream, logp,
+                       ids, root, L, k, k_tree, budget, lay.cand_cap, n_nodes, token, parent,
+                       depth, score, mask);
+  else
+    hipLaunchKernelGGL(tree_kernel<false>, dim3(batch), dim3(threads), lay.bytes, stream, logp,
+                       ids, root, L, k, k_tree, budget, lay.cand_cap, n_nodes, token, parent,
+                       depth, score, mask);
   return hipGetLastError();
 }
 
