@@ -243,9 +243,10 @@ __global__ __launch_bounds__(1024) void tree_kernel(
           const int cnt = __builtin_amdgcn_readlane(wave_inclusive_scan(c_l), kWave - 1);
           if (lane == 0) wcnt[round * 64 + wid] = cnt;
           __syncthreads();
-          int k = -1;
-          for (int w = 0; w < nwaves; ++w)
-            if (wcnt[round * 64 + w] >= B) k = w;
+          // the highest probe that keeps B candidates: counts fall with the
+          // probe, so it is the last lane of a ballot over the probe counts
+          const uint64_t keep = __ballot(lane < nwaves && wcnt[round * 64 + lane] >= B);
+          const int k = keep ? 63 - __builtin_clzll(keep) : -1;
           const float t_lo = k >= 0 ? lo_f + (hi_f - lo_f) * (float)(k + 1) / (float)(nwaves + 1)
                                     : lo_f;
           const float t_hi = k + 1 < nwaves
