@@ -802,6 +802,13 @@ AttnPlan attn_plan(int batch, int hq, int hkv, int n_q_max, int max_kv_len) {
     if (s > by_tiles) s = by_tiles;
     while (s > 1 && heavy * s + tail * tail_split((int)s) > kCUs) --s;
     plan.n_split = clamp_split(s);
+    // Several requests decode split fastest over the XCDs (a workgroup's XCD
+    // is its triple index mod 8): an even split count would tie split s to
+    // the XCDs of its residue, and since a short request leaves its last
+    // splits empty, those XCDs would idle while the first ones queue the
+    // long requests' work (measured: a ragged batch at 8 splits took 1.5x
+    // its 9-split time).  An odd count walks every split over every XCD.
+    if (batch > 1 && plan.n_split % 2 == 0 && plan.n_split < max_tiles) ++plan.n_split;
     plan.n_split_tail = tail_split(plan.n_split);
   } else {
     // only a partial group per head (drafter-sized queries): half a
