@@ -89,6 +89,7 @@ namespace {
 // most one candidate per thread, or more than this many, take the
 // merge-path rounds).
 constexpr int kMaxCarry = 8;
+constexpr int kBuckets = 2048;  // buckets of the per-level sort (<= 64 x 34 - 1)
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & (kWave - 1);
@@ -320,93 +321,85 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     }
     for (int j = tid; j <= n + 1; j += nt)  // offsets of runs 0..n, and the end
       roff[j] = j == 0 ? 0 : (j <= n ? g + rcnt[j - 1] : g + nc);
+    for (int b = tid; b <= kBuckets; b += nt) wcnt[b] = 0;  // bucket counts of the sort below
     __syncthreads();
     const int total = g + nc;
-    if (total > nt && total <= kMaxCarry * nt) {
-      // Several elements per thread: pairwise rounds, runs (2i, 2i+1) ->
-      // run i, each element placed by its own thread.  Element e of
-      // [0, total) stays with thread e % nt (slot e / nt) for every round,
-      // its key in registers; its index in the merged run is its index in
-      // its own run plus the number of keys of the partner run above it
-      // (keys are distinct: depth, parent and rank are part of them), one
-      // binary search.  A merged run keeps its left run's start and at most
-      // B elements: an element with B or more keys above it in any subset
-      // cannot be in the top B, and neither can anything below it, so it
-      // drops out, and later rounds move fewer elements.
+    if (total <= kMaxCarry * nt) {
+      // Top B of G and the runs by one bucket pass instead of merge rounds:
+      // element e of [0, total) stays with thread e % nt (slot e / nt).
+      // Its bucket falls with its score (linear in the score between the
+      // level's extremes, so equal scores share a bucket); an atomic count
+      // gives it a slot in its bucket; after a scan of the counts the keys
+      // are scattered by (bucket start + slot), and each element's place is
+      // its bucket's start plus the keys of its bucket above its own (keys
+      // are distinct: depth, parent and rank are part of them).  Places
+      // from B on are dropped.  Four barriers after the children's, where
+      // pairwise merging takes one per round and a binary search per
+      // element each round.
+      int* bstart = wcnt;  // kBuckets + 1 counts, zeroed with the children
+      // the extremes: the first and last key of every run (each wave alike)
+      float smax = -INFINITY, smin = INFINITY;
+      for (int i = lane; i <= n; i += kWave) {
+        if (roff[i + 1] > roff[i]) {
+          smax = fmaxf(smax, key_score(gb[roff[i]]));
+          smin = fminf(smin, key_score(gb[roff[i + 1] - 1]));
+        }
+      }
+      smax = wave_max_f(smax);
+      smin = -wave_max_f(-smin);
+      const float bscale = smax > smin ? (float)(kBuckets - 1) / (smax - smin) : 0.f;
+      const int M = (total + nt - 1) / nt;  // slots in use (uniform)
       uint64_t xk[kMaxCarry];
-      int xrun[kMaxCarry], xidx[kMaxCarry];
+      int xb[kMaxCarry], xs[kMaxCarry];
 #pragma unroll
       for (int m = 0; m < kMaxCarry; ++m) {
-        const int e = tid + m * nt;
-        xrun[m] = -1;
-        xidx[m] = 0;
+        xb[m] = -1;
+        xs[m] = 0;
         xk[m] = 0ull;
+        if (m >= M) continue;
+        const int e = tid + m * nt;
         if (e < total) {
-          const uint64_t x = gb[e];
-          xk[m] = x;
-          // G is run 0; a child's run (parent j + 1) and index (its rank)
-          // are in its key
-          const int pr = key_pr(x);
-          xrun[m] = e < g ? 0 : (pr >> 7) + 1;
-          xidx[m] = e < g ? e : (pr & 127);
+          xk[m] = gb[e];
+          // bucket 0 holds the highest scores
+          int bk = (int)((smax - key_score(xk[m])) * bscale);
+          bk = bk < 0 ? 0 : (bk > kBuckets - 1 ? kBuckets - 1 : bk);
+          xb[m] = bk;
+          xs[m] = atomicAdd(&bstart[bk], 1);
         }
       }
-      // run lengths after the first round (which takes them from the
-      // offsets), in the parent-score / run-count / slot arrays (3 Bp ints,
-      // free until the next level): at most (B + 2) / 2, then half as many
-      // for the round after, ping-ponged
-      int* rl = nullptr;
-      int* rl_next = reinterpret_cast<int*>(pscore);
-      int* rl_spare = rl_next + (B + 2) / 2 + 1;
-      int R = n + 1;
-      uint64_t* src = gb;
-      uint64_t* dst = obuf;
-      int* rs = roff;
-      int* rs_next = roff2;
-      while (R > 1) {
-        const int Rn = (R + 1) >> 1;
+      __syncthreads();
+      // exclusive scan of the counts by one wave, kBuckets / 64 per lane;
+      // bstart[kBuckets] = total
+      if (wid == 0) {
+        constexpr int kPer = kBuckets / kWave;
+        int* mine = bstart + lane * kPer;
+        int sum = 0;
 #pragma unroll
-        for (int m = 0; m < kMaxCarry; ++m) {
-          const int i = xrun[m];
-          if (i < 0) continue;
-          const int pi = i ^ 1;
-          int above = 0;
-          if (pi < R) {
-            const int b0 = rs[pi];
-            int lo = 0, hi = rl != nullptr ? rl[pi] : rs[pi + 1] - b0;
-            while (lo < hi) {
-              const int mid = (lo + hi) >> 1;
-              if (src[b0 + mid] > xk[m]) lo = mid + 1;
-              else hi = mid;
-            }
-            above = lo;
-          }
-          const int ni = xidx[m] + above;
-          if (ni >= B) {
-            xrun[m] = -1;
-          } else {
-            dst[rs[i & ~1] + ni] = xk[m];
-            xrun[m] = i >> 1;
-            xidx[m] = ni;
-          }
+        for (int t = 0; t < kPer; ++t) sum += mine[t];
+        int run = wave_inclusive_scan(sum) - sum;
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+          const int c = mine[t];
+          mine[t] = run;
+          run += c;
         }
-        for (int k = tid; k < Rn; k += nt) {
-          rs_next[k] = rs[2 * k];
-          const int la = rl != nullptr ? rl[2 * k] : rs[2 * k + 1] - rs[2 * k];
-          const int lb = 2 * k + 1 >= R ? 0
-                         : (rl != nullptr ? rl[2 * k + 1] : rs[2 * k + 2] - rs[2 * k + 1]);
-          rl_next[k] = la + lb < B ? la + lb : B;
-        }
-        __syncthreads();
-        uint64_t* t = src; src = dst; dst = t;
-        int* u = rs; rs = rs_next; rs_next = u;
-        int* w = rl_next;
-        rl_next = rl != nullptr ? rl : rl_spare;
-        rl = w;
-        R = Rn;
+        if (lane == kWave - 1) bstart[kBuckets] = run;
       }
-      gb = src;
-      obuf = dst;
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < kMaxCarry; ++m)
+        if (m < M && xb[m] >= 0) obuf[bstart[xb[m]] + xs[m]] = xk[m];
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < kMaxCarry; ++m) {
+        if (m >= M || xb[m] < 0) continue;
+        const int s0 = bstart[xb[m]], s1 = bstart[xb[m] + 1];
+        int above = 0;
+        for (int j = s0; j < s1; ++j) above += obuf[j] > xk[m] ? 1 : 0;
+        const int pos = s0 + above;
+        if (pos < B) gb[pos] = xk[m];
+      }
+      __syncthreads();
     } else {
       // pairwise merge-path rounds: runs (2i, 2i+1) -> run i, every output
       // element placed independently by a binary search on its diagonal
