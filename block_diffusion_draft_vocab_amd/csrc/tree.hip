@@ -368,32 +368,45 @@ __global__ __launch_bounds__(1024) void tree_kernel(
         }
       }
       __syncthreads();
-      // exclusive scan of the counts by one wave, kBuckets / 64 per lane;
-      // bstart[kBuckets] = total
-      if (wid == 0) {
-        constexpr int kPer = kBuckets / kWave;
-        int* mine = bstart + lane * kPer;
-        int sum = 0;
-#pragma unroll
-        for (int t = 0; t < kPer; ++t) sum += mine[t];
-        int run = wave_inclusive_scan(sum) - sum;
-#pragma unroll
-        for (int t = 0; t < kPer; ++t) {
-          const int c = mine[t];
-          mine[t] = run;
-          run += c;
+      // exclusive scan of the counts: wave w turns its segment of kBuckets /
+      // nwaves buckets (rows of 64, read coalesced) into prefixes within the
+      // segment and leaves the segment's total; a bucket's start is that
+      // prefix plus the totals of the segments before it
+      const int seg = kBuckets / nwaves;  // nwaves <= 16: 1024 threads at most
+      {
+        int run = 0;
+        for (int r0 = 0; r0 < seg; r0 += kWave) {
+          const int b = wid * seg + r0 + lane;
+          const int c = bstart[b];
+          const int inc = wave_inclusive_scan(c);
+          bstart[b] = run + inc - c;
+          run += __builtin_amdgcn_readlane(inc, kWave - 1);
         }
-        if (lane == kWave - 1) bstart[kBuckets] = run;
+        if (lane == 0) misc[8 + wid] = run;
       }
       __syncthreads();
+      // every element's bucket range [start, end), with all lanes active
+      // (the shuffle reads lanes that the branches below would mask off):
+      // the segment's prefix plus the totals of the segments before it
+      const int tot_lane = lane < nwaves ? misc[8 + lane] : 0;
+      const int seg_before = wave_inclusive_scan(tot_lane) - tot_lane;  // lane nwaves: total
+      int xs0[kMaxCarry], xs1[kMaxCarry];
+#pragma unroll
+      for (int m = 0; m < kMaxCarry; ++m) {
+        xs0[m] = xs1[m] = 0;
+        if (m >= M) continue;
+        const int b = xb[m] < 0 ? 0 : xb[m];
+        xs0[m] = bstart[b] + __shfl(seg_before, b / seg, kWave);
+        xs1[m] = (b + 1 < kBuckets ? bstart[b + 1] : 0) + __shfl(seg_before, (b + 1) / seg, kWave);
+      }
 #pragma unroll
       for (int m = 0; m < kMaxCarry; ++m)
-        if (m < M && xb[m] >= 0) obuf[bstart[xb[m]] + xs[m]] = xk[m];
+        if (m < M && xb[m] >= 0) obuf[xs0[m] + xs[m]] = xk[m];
       __syncthreads();
 #pragma unroll
       for (int m = 0; m < kMaxCarry; ++m) {
         if (m >= M || xb[m] < 0) continue;
-        const int s0 = bstart[xb[m]], s1 = bstart[xb[m] + 1];
+        const int s0 = xs0[m], s1 = xs1[m];
         int above = 0;
         for (int j = s0; j < s1; ++j) above += obuf[j] > xk[m] ? 1 : 0;
         const int pos = s0 + above;
