@@ -15,7 +15,10 @@
 //     children (j, rank) with key > theta and (j+1)(rank+1) <= B; the
 //       children of one parent form a descending run, whose length a binary
 //       search over the ranks finds
-//     G := top B of (G u runs), merged by pairwise merge-path rounds
+//     G := top B of (G u runs), sorted: a bucket pass by score (atomic slot
+//       per bucket, scan of the counts, scatter, rank within the bucket by
+//       the full key) when the level has at most 8 candidates per thread,
+//       pairwise merge-path rounds otherwise
 //     theta := G[B-1]
 //
 // Why it is exact: a node's key is below its parent's and its elder
@@ -96,10 +99,6 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (kWave - lane));
 }
 
-// kPrune: levels with many candidates per thread narrow theta first (the
-// launch picks it from the depth-2 candidate bound; a kernel without that
-// code stays smaller, which the single-workgroup budget-256 tree notices).
-template <bool kPrune>
 __global__ __launch_bounds__(1024) void tree_kernel(
     const float* __restrict__ logp, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ root_token, int L, int K, int k_tree, int B, int cand_cap,
@@ -188,79 +187,6 @@ __global__ __launch_bounds__(1024) void tree_kernel(
         if (key_depth(kq) == d - 1) pscore[pre + slot_tab[q]] = key_score(kq);
       }
       __syncthreads();
-    }
-    // With kPrune, a level with many candidates per thread first narrows
-    // theta: a
-    // score s_lo with at least B candidates at or above it bounds the B-th
-    // key from below, so children below s_lo can be left out before the
-    // merge (the merge cut at B stays exact).  The candidates are G and the
-    // children (j, c) with c < min(k_tree, B / (j + 1)); each wave counts
-    // those at or above one probe score (parents spread over its lanes, G
-    // in 64 slices), and every round keeps the highest probe that still
-    // has B candidates, until at most B + B/4 remain above the bound.
-    if constexpr (kPrune) {
-      // bound on the candidate count (no pass over the parents): the first
-      // m0 = min(n, B / k_tree) parents give k_tree children each, parent j
-      // beyond them at most B / (j + 1) <= B / (m0 + 1) + B ln(n / (m0 + 1)) in all
-      const int m0 = min(n, B / k_tree);
-      const float tail_ub = n > m0 ? (float)B / (float)(m0 + 1) +
-                                         (float)B * __logf((float)n / (float)(m0 + 1))
-                                   : 0.f;
-      const int est = g + m0 * k_tree + (int)tail_ub + 1;
-      if (est > nt && est > 2 * B) {
-        auto ps_of = [&](int j) { return d == 2 ? 0.0f + y[j] : pscore[j]; };
-        // lowest candidate score: the last child of every parent, and G's last
-        float mn = key_score(gb[g - 1]);
-        for (int j = lane; j < n; j += kWave)
-          mn = fminf(mn, ps_of(j) + yd[min(k_tree, B / (j + 1)) - 1]);
-        float lo_f = -wave_max_f(-mn);
-        float hi_f = best_child;
-        int cnt_lo = est;
-        const int seg = (g + kWave - 1) / kWave;
-        for (int round = 0; round < 4 && cnt_lo > B + B / 4; ++round) {
-          const float t = lo_f + (hi_f - lo_f) * (float)(wid + 1) / (float)(nwaves + 1);
-          int c_l = 0;
-          for (int j = lane; j < n; j += kWave) {
-            const float ps = ps_of(j);
-            int lo = 0, hi = min(k_tree, B / (j + 1));
-            while (lo < hi) {
-              const int mid = (lo + hi) >> 1;
-              if (ps + yd[mid] >= t) lo = mid + 1;
-              else hi = mid;
-            }
-            c_l += lo;
-          }
-          {  // G slice [lane * seg, lane * seg + seg), scores non-increasing
-            int lo = lane * seg < g ? lane * seg : g;
-            int hi = lo + seg < g ? lo + seg : g;
-            const int b = lo;
-            while (lo < hi) {
-              const int mid = (lo + hi) >> 1;
-              if (key_score(gb[mid]) >= t) lo = mid + 1;
-              else hi = mid;
-            }
-            c_l += lo - b;
-          }
-          const int cnt = __builtin_amdgcn_readlane(wave_inclusive_scan(c_l), kWave - 1);
-          if (lane == 0) wcnt[round * 64 + wid] = cnt;
-          __syncthreads();
-          // the highest probe that keeps B candidates: counts fall with the
-          // probe, so it is the last lane of a ballot over the probe counts
-          const uint64_t keep = __ballot(lane < nwaves && wcnt[round * 64 + lane] >= B);
-          const int k = keep ? 63 - __builtin_clzll(keep) : -1;
-          const float t_lo = k >= 0 ? lo_f + (hi_f - lo_f) * (float)(k + 1) / (float)(nwaves + 1)
-                                    : lo_f;
-          const float t_hi = k + 1 < nwaves
-                                 ? lo_f + (hi_f - lo_f) * (float)(k + 2) / (float)(nwaves + 1)
-                                 : hi_f;
-          if (k >= 0) cnt_lo = wcnt[round * 64 + k];
-          lo_f = t_lo;
-          hi_f = t_hi;
-        }
-        // children with a score >= lo_f have keys above this bound
-        const uint64_t bound = ((uint64_t)f32_order(0.0f + lo_f) << 32) - 1ull;
-        if (bound > theta) theta = bound;
-      }
     }
     // run length of parent j: children (j, c) with key above theta and
     // (j+1)(c+1) <= B; keys fall with c, so a binary search finds it.
@@ -594,25 +520,12 @@ hipError_t launch_tree(const float* logp, const int32_t* ids, const int32_t* roo
   // enough threads for one merge element per thread at the common sizes
   int threads = 256;
   while (threads < 1024 && threads < lay.cand_cap) threads <<= 1;
-  // depth 2 has the most candidates per parent: all min(k_tree, B) depth-1
-  // nodes are parents, parent j with at most min(k_tree, B / (j + 1))
-  // children
-  const int n2 = k_tree < budget ? k_tree : budget;
-  long cand2 = n2;
-  for (int j = 0; j < n2; ++j) cand2 += k_tree < budget / (j + 1) ? k_tree : budget / (j + 1);
-  const bool prune = L > 1 && cand2 > threads && cand2 > 2L * budget;
-  const void* fn = prune ? reinterpret_cast<const void*>(tree_kernel<true>)
-                         : reinterpret_cast<const void*>(tree_kernel<false>);
   if (lay.bytes > 64 * 1024)
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
-  if (prune)
-    hipLaunchKernelGGL(tree_kernel<true>, dim3(batch), dim3(threads), lay.bytes, stream, logp,
-                       ids, root, L, k, k_tree, budget, lay.cand_cap, n_nodes, token, parent,
-                       depth, score, mask);
-  else
-    hipLaunchKernelGGL(tree_kernel<false>, dim3(batch), dim3(threads), lay.bytes, stream, logp,
-                       ids, root, L, k, k_tree, budget, lay.cand_cap, n_nodes, token, parent,
-                       depth, score, mask);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(tree_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
+  hipLaunchKernelGGL(tree_kernel, dim3(batch), dim3(threads), lay.bytes, stream, logp, ids,
+                     root, L, k, k_tree, budget, lay.cand_cap, n_nodes, token, parent, depth,
+                     score, mask);
   return hipGetLastError();
 }
 
