@@ -188,66 +188,98 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       }
       __syncthreads();
     }
-    // run length of parent j: children (j, c) with key above theta and
-    // (j+1)(c+1) <= B; keys fall with c, so a binary search finds it.
-    // Thread t owns parents [t*per, t*per + per).
-    // (n <= B < 2 * nt: the launch gives max(cand_cap, 1024) threads or more)
-    const int per = (n + nt - 1) / nt;
-    int lens[2] = {0, 0};
-    int mine = 0;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = tid * per + u;
-      int len = 0;
-      if (u < per && j < n) {
-        int lo = 0, hi = min(k_tree, B / (j + 1));
-        float ps;
-        if (d == 2) {
-          ps = 0.0f + y[j];  // the key of G[j], exactly
-          pscore[j] = ps;    // read by the children pass, after a barrier
-        } else {
-          ps = pscore[j];
-        }
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (tkey(ps + yd[mid], d, j, mid) > theta) lo = mid + 1;
-          else hi = mid;
-        }
-        len = lo;
+    int nc;
+    if (theta == 0ull && n <= kWave) {
+      // No bound from G yet (fewer than B keys so far): every child with
+      // (j+1)(c+1) <= B is a candidate, so parent j's run holds
+      // min(k_tree, B / (j + 1)) children and the run offsets are one wave
+      // scan, done by every wave alike: no search, no barrier.  The shuffles
+      // run with every lane active (a uniform trip count).
+      const int lenj = lane < n ? min(k_tree, B / (lane + 1)) : 0;
+      const int incj = wave_inclusive_scan(lenj);
+      nc = __builtin_amdgcn_readlane(incj, kWave - 1);
+      if (nc == 0) break;
+      const float psj = lane < n ? (d == 2 ? 0.0f + y[lane] : pscore[lane]) : 0.f;
+      const int exj = incj - lenj;
+      const int items = n * k_tree;
+      for (int base = 0; base < items; base += nt) {
+        const int it = base + tid;
+        const int j = it < items ? it / k_tree : 0;
+        const int c = it - j * k_tree;
+        const int len = __shfl(lenj, j, kWave);
+        const int o = __shfl(exj, j, kWave);
+        const float ps = __shfl(psj, j, kWave);
+        if (it < items && c < len) gb[g + o + c] = tkey(ps + yd[c], d, j, c);
       }
-      lens[u] = len;
-      mine += len;
-    }
-    // block exclusive scan of the per-thread totals
-    const int inc = wave_inclusive_scan(mine);
-    if (lane == kWave - 1) misc[8 + wid] = inc;
-    __syncthreads();
-    const int winc = wave_inclusive_scan(lane < nwaves ? misc[8 + lane] : 0);
-    const int wpre = wid > 0 ? __builtin_amdgcn_readlane(winc, wid - 1) : 0;
-    const int nc = __builtin_amdgcn_readlane(winc, kWave - 1);
-    {
-      int o = wpre + inc - mine;
+      // run starts: G at 0, parent j's run at g + its prefix, and the end
+      if (lane < n) roff[1 + lane] = g + exj;
+      if (lane == 0) {
+        roff[0] = 0;
+        roff[n + 1] = g + nc;
+      }
+      for (int b = tid; b <= kBuckets; b += nt) wcnt[b] = 0;  // bucket counts of the sort below
+    } else {
+      // run length of parent j: children (j, c) with key above theta and
+      // (j+1)(c+1) <= B; keys fall with c, so a binary search finds it.
+      // Thread t owns parents [t*per, t*per + per).
+      // (n <= B < 2 * nt: the launch gives max(cand_cap, 1024) threads or more)
+      const int per = (n + nt - 1) / nt;
+      int lens[2] = {0, 0};
+      int mine = 0;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j = tid * per + u;
-        if (u < per && j < n) rcnt[j] = o;
-        o += lens[u];
+        int len = 0;
+        if (u < per && j < n) {
+          int lo = 0, hi = min(k_tree, B / (j + 1));
+          float ps;
+          if (d == 2) {
+            ps = 0.0f + y[j];  // the key of G[j], exactly
+            pscore[j] = ps;    // read by the children pass, after a barrier
+          } else {
+            ps = pscore[j];
+          }
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (tkey(ps + yd[mid], d, j, mid) > theta) lo = mid + 1;
+            else hi = mid;
+          }
+          len = lo;
+        }
+        lens[u] = len;
+        mine += len;
       }
+      // block exclusive scan of the per-thread totals
+      const int inc = wave_inclusive_scan(mine);
+      if (lane == kWave - 1) misc[8 + wid] = inc;
+      __syncthreads();
+      const int winc = wave_inclusive_scan(lane < nwaves ? misc[8 + lane] : 0);
+      const int wpre = wid > 0 ? __builtin_amdgcn_readlane(winc, wid - 1) : 0;
+      nc = __builtin_amdgcn_readlane(winc, kWave - 1);
+      {
+        int o = wpre + inc - mine;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = tid * per + u;
+          if (u < per && j < n) rcnt[j] = o;
+          o += lens[u];
+        }
+      }
+      if (nc == 0) break;
+      __syncthreads();
+      // children keys after G: run 0 = G at [0, g), run j+1 = parent j's
+      const int items = n * k_tree;
+      for (int it = tid; it < items; it += nt) {
+        const int j = it / k_tree;
+        const int c = it - j * k_tree;
+        const int o = rcnt[j];
+        const int len = (j + 1 < n ? rcnt[j + 1] : nc) - o;
+        if (c < len) gb[g + o + c] = tkey(pscore[j] + yd[c], d, j, c);
+      }
+      for (int j = tid; j <= n + 1; j += nt)  // offsets of runs 0..n, and the end
+        roff[j] = j == 0 ? 0 : (j <= n ? g + rcnt[j - 1] : g + nc);
+      for (int b = tid; b <= kBuckets; b += nt) wcnt[b] = 0;  // bucket counts of the sort below
     }
-    if (nc == 0) break;
-    __syncthreads();
-    // children keys after G: run 0 = G at [0, g), run j+1 = parent j's
-    const int items = n * k_tree;
-    for (int it = tid; it < items; it += nt) {
-      const int j = it / k_tree;
-      const int c = it - j * k_tree;
-      const int o = rcnt[j];
-      const int len = (j + 1 < n ? rcnt[j + 1] : nc) - o;
-      if (c < len) gb[g + o + c] = tkey(pscore[j] + yd[c], d, j, c);
-    }
-    for (int j = tid; j <= n + 1; j += nt)  // offsets of runs 0..n, and the end
-      roff[j] = j == 0 ? 0 : (j <= n ? g + rcnt[j - 1] : g + nc);
-    for (int b = tid; b <= kBuckets; b += nt) wcnt[b] = 0;  // bucket counts of the sort below
     __syncthreads();
     const int total = g + nc;
     if (total <= kMaxCarry * nt) {
