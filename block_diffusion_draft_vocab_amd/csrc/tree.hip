@@ -149,6 +149,7 @@ __global__ __launch_bounds__(1024) void tree_kernel(
   // level's first parent (depth 1: rank 0 of row 0)
   float best_prev = 0.0f + y[0];
 
+  int dmax = 1;  // deepest level that added nodes
   for (int d = 2; d <= L && g > 0; ++d) {
     // The level's best possible child is the rank-0 child of its first
     // parent (the best depth-(d-1) node, which is in G: it beat theta when
@@ -414,52 +415,46 @@ __global__ __launch_bounds__(1024) void tree_kernel(
     }
     g = min(B, total);
     theta = (g == B) ? gb[B - 1] : 0ull;
+    dmax = d;
   }
   __syncthreads();
   keys = gb;
 
   // ---- flatten: slot of every node, parent slots, outputs, ancestor mask
-  // level-local index of every node within its depth, all depths at once:
-  // per chunk of 64 positions one ballot per depth, then a prefix per depth
+  // level-local index of every node within its depth, depths 1..dmax at
+  // once: per chunk of 64 positions one ballot per depth (every count
+  // written, zeros included); then one wave, a lane per depth, turns the
+  // counts into per-chunk prefixes and the depths' offsets; then every node
+  // takes its depth-major position and writes itself into the inverse table
   {
     const int nchunk = (g + kWave - 1) / kWave;
-    for (int i = tid; i < nchunk * 34; i += nt) wcnt[i] = 0;
-    __syncthreads();
     for (int c = wid; c < nchunk; c += nt / kWave) {
       const int q = c * kWave + lane;
       const int dq = q < g ? key_depth(keys[q]) : 0;
-      for (int dd = 1; dd <= L; ++dd) {
+      for (int dd = 1; dd <= dmax; ++dd) {
         const uint64_t bal = __ballot(dq == dd);
-        if (bal == 0) continue;
         if (lane == 0) wcnt[c * 34 + dd] = __popcll(bal);
         if (dq == dd) slot_tab[q] = __popcll(bal & lanemask_lt());
       }
     }
     __syncthreads();
-    if (tid < 34) {
-      const int dd = tid;
-      int run = 0;
-      for (int c = 0; c < nchunk; ++c) {
-        const int t = wcnt[c * 34 + dd];
-        wcnt[c * 34 + dd] = run;
-        run += t;
-      }
-      dcount[dd] = run;
-    }
-    __syncthreads();
     if (tid < kWave) {
-      const int t = tid < 34 ? dcount[tid] : 0;
-      const int inc = wave_inclusive_scan(t);
-      if (tid < 34) doff[tid] = inc - t;
+      int run = 0;
+      if (tid >= 1 && tid <= dmax) {
+        for (int c = 0; c < nchunk; ++c) {
+          const int t = wcnt[c * 34 + tid];
+          wcnt[c * 34 + tid] = run;
+          run += t;
+        }
+      }
+      const int inc = wave_inclusive_scan(run);
+      if (tid < 34) doff[tid] = inc - run;
     }
     __syncthreads();
     for (int q = tid; q < g; q += nt) {
       const int dq = key_depth(keys[q]);
-      slot_tab[q] = doff[dq] + wcnt[(q / kWave) * 34 + dq] + slot_tab[q];
+      roff[doff[dq] + wcnt[(q / kWave) * 34 + dq] + slot_tab[q]] = q + 1;
     }
-    __syncthreads();
-    // slot_tab[q] = position of node q in the depth-major order; invert it
-    for (int q = tid; q < g; q += nt) roff[slot_tab[q]] = q + 1;
     __syncthreads();
   }
   if (tid == 0) par_slot[0] = -1;
