@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   __shared__ uint64_t win_lds[kMaxTilesPerSplit][kColsPerWG];  // own-row tile windows
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int h2 = lane >> 5;
   const int n = lane & 31;
 
@@ -367,8 +367,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int row_stride = p.hkv * D;  // elements; a request's rows span < 2^31 elements
   const uint16_t* kbase = p.k + base * row_stride + (int64_t)hk * D;
   const uint16_t* vbase = p.v + base * row_stride + (int64_t)hk * D;
+  // The per-thread part of each copy's address is the same for every tile
+  // and computed here once: a tile's copies then cost one scalar base each,
+  // plus a clamp of the rows past the request's last key in its final tile.
   int ld_row[G::kLoads];
   int ld_col[G::kLoads];       // element offset of the logical chunk
+  uint32_t ld_off[G::kLoads];  // byte offset of the copy inside a whole tile
   uint32_t ld_lds[G::kLoads];  // wave-uniform LDS offset inside one slot pair
   constexpr int kPer = kKT * G::kCh;
 #pragma unroll
@@ -378,19 +382,36 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     const int Lt = isv ? L - kPer : L;
     ld_row[j] = Lt / G::kCh;
     ld_col[j] = ((Lt % G::kCh) ^ (isv ? G::swz_v(ld_row[j]) : G::swz_k(ld_row[j]))) * 8;
-    ld_lds[j] = (uint32_t)((Lt - lane) * 16) + (isv ? kRing * G::kTileBytes : 0);
+    ld_off[j] = (uint32_t)(ld_row[j] * row_stride + ld_col[j]) * 2u;
+    ld_lds[j] = __builtin_amdgcn_readfirstlane((Lt - lane) * 16) +
+                (isv ? kRing * G::kTileBytes : 0);
   }
   auto issue_tile = [&](int t, int slot) {
     const int key0 = t * kKT;
-    const int last = T - 1 - key0;  // rows past the end copy a valid row, never visible
+    const uint32_t slot_lds = lds0 + slot * G::kTileBytes;
+    if (key0 + kKT <= T) {
 #pragma unroll
-    for (int j = 0; j < G::kLoads; ++j) {
-      const bool isv = G::kLoads == 1 ? wid >= 4 : j >= G::kLoads / 2;
-      const uint16_t* tb = (isv ? vbase : kbase) + (int64_t)key0 * row_stride;
-      const int row = ld_row[j] < last ? ld_row[j] : last;
-      const uint16_t* src = tb + (row * row_stride + ld_col[j]);
-      const uint32_t dst = lds0 + slot * G::kTileBytes + ld_lds[j];
-      __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)dst, 16, 0, 0);
+      for (int j = 0; j < G::kLoads; ++j) {
+        const bool isv = G::kLoads == 1 ? wid >= 4 : j >= G::kLoads / 2;
+        // (the source goes through a named pointer: passed as an expression,
+        // the host compilation pass drops the kernel's launch stub)
+        const char* src =
+            reinterpret_cast<const char*>((isv ? vbase : kbase) + (int64_t)key0 * row_stride) +
+            ld_off[j];
+        __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)(slot_lds + ld_lds[j]), 16,
+                                         0, 0);
+      }
+    } else {
+      const int last = T - 1 - key0;  // rows past the end copy a valid row, never visible
+#pragma unroll
+      for (int j = 0; j < G::kLoads; ++j) {
+        const bool isv = G::kLoads == 1 ? wid >= 4 : j >= G::kLoads / 2;
+        const uint16_t* tb = (isv ? vbase : kbase) + (int64_t)key0 * row_stride;
+        const int row = ld_row[j] < last ? ld_row[j] : last;
+        const uint16_t* src = tb + (row * row_stride + ld_col[j]);
+        __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)(uintptr_t)(slot_lds + ld_lds[j]), 16,
+                                         0, 0);
+      }
     }
   };
 
@@ -452,7 +473,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     __syncthreads();
     ntl = n_tiles_s;
   }
-  auto tile_at = [&](int i) { return listed ? tile_list[i] : t_begin + i; };
+  auto tile_at = [&](int i) {
+    return listed ? __builtin_amdgcn_readfirstlane(tile_list[i]) : t_begin + i;
+  };
 
   // ---- per-lane LDS read offsets inside one slot.
   // K as the A operand of S^T: row n (+32 for the second half), logical
