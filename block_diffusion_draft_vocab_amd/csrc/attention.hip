@@ -671,19 +671,38 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // D/8 lanes per row, 64 / (D/8) rows per instruction
+  // D/8 lanes per row, 64 / (D/8) rows per instruction.  The element offset
+  // of the row a lane stores is stepped from one division up front (with a
+  // division per store, the address arithmetic rather than the stores set
+  // the time of this loop), and every staged row is read before the stores.
   constexpr int kLpr = D / 8;
   constexpr int kRpi = 64 / kLpr;
+  const int chunk = lane % kLpr;
+  u32x4 rv[kColsPerWave / kRpi];
+#pragma unroll
+  for (int rr = 0; rr < kColsPerWave; rr += kRpi)
+    rv[rr / kRpi] =
+        *(const LDS_AS u32x4*)(uintptr_t)(stage + (rr + lane / kLpr) * kRowPad + chunk * 16);
+  const int cfirst = col0 + wid * kColsPerWave + lane / kLpr;
+  const int q0 = cfirst / g;
+  int ho = cfirst - q0 * g;
+  const int dq = kRpi / g, dh = kRpi - dq * g;
+  const int64_t ostride = SPLIT ? (int64_t)p.n_split * D : (int64_t)D;  // elements per row id
+  int64_t eoff = (((int64_t)r * p.n_q_max + q0) * p.hq + hk * g + ho) * ostride +
+                 (SPLIT ? (int64_t)s * D : 0) + chunk * 8;
+  const int64_t step = (int64_t)(dq * p.hq + dh) * ostride;
+  const int64_t wrap = (int64_t)(p.hq - g) * ostride;
 #pragma unroll
   for (int rr = 0; rr < kColsPerWave; rr += kRpi) {
-    const int row = rr + lane / kLpr;
-    const int chunk = lane % kLpr;
-    const int c = col0 + wid * kColsPerWave + row;
-    const u32x4 v = *(const LDS_AS u32x4*)(uintptr_t)(stage + row * kRowPad + chunk * 16);
-    if (c < ncols) {
-      const int64_t rowid = ((int64_t)r * p.n_q_max + c / g) * p.hq + hk * g + c % g;
-      if constexpr (SPLIT) store_partial16(p.part_o + (rowid * p.n_split + s) * D + chunk * 8, v);
-      else *reinterpret_cast<u32x4*>(p.out + rowid * D + chunk * 8) = v;
+    if (cfirst + rr < ncols) {
+      if constexpr (SPLIT) store_partial16(p.part_o + eoff, rv[rr / kRpi]);
+      else *reinterpret_cast<u32x4*>(p.out + eoff) = rv[rr / kRpi];
+    }
+    eoff += step;
+    ho += dh;
+    if (ho >= g) {
+      ho -= g;
+      eoff += wrap;
     }
   }
 }
