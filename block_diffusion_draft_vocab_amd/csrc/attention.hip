@@ -125,8 +125,25 @@ __device__ __forceinline__ void split_range(int s, int n_split, int nt, int& t0,
 // ragged batch gets splits of about the same length as the longest one
 // (never more tiles per split than the plan allows: ns >= max_tiles / 16).
 __device__ __forceinline__ int request_splits(int ns, int nt, int max_tiles) {
-  const long v = ((long)nt * ns + max_tiles - 1) / max_tiles;
+  if (nt >= max_tiles) return ns;
+  // 32-bit arithmetic whenever the product fits (a 64-bit division is a long
+  // instruction sequence at the head of every workgroup)
+  const long v = max_tiles <= 0xFFFF
+                     ? (long)(((uint32_t)nt * (uint32_t)ns + (uint32_t)max_tiles - 1u) /
+                              (uint32_t)max_tiles)
+                     : ((long)nt * ns + max_tiles - 1) / max_tiles;
   return v < 1 ? 1 : (v > ns ? ns : (int)v);
+}
+// x / d and x % d for x >= 0 and d > 0 uniform: a shift and a mask when d is
+// a power of two (the usual q-heads per KV head), else the division.
+__device__ __forceinline__ int divmod_u(int x, int d, int& rem) {
+  if ((d & (d - 1)) == 0) {
+    rem = x & (d - 1);
+    return x >> __builtin_ctz((unsigned)d);
+  }
+  const int q = (int)((unsigned)x / (unsigned)d);
+  rem = x - q * d;
+  return q;
 }
 // Split s is empty only when there are fewer tiles than splits.
 __device__ __forceinline__ bool split_nonempty(int s, int n_split, int nt) {
@@ -305,19 +322,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int max_split = p.n_split > p.n_split_tail ? p.n_split : p.n_split_tail;
   const int xcd = blockIdx.x % kXcds;
   const int jx = blockIdx.x / kXcds;
-  const int cg = jx % n_groups;
-  int x = (jx / n_groups) * kXcds + xcd;
+  int cg;
+  int x = divmod_u(jx, n_groups, cg) * kXcds + xcd;
   int s, hk, r;
   if (p.batch == 1) {
-    hk = x % p.hkv;
     r = 0;
-    s = x / p.hkv;
+    s = divmod_u(x, p.hkv, hk);
     if (s >= max_split) return;  // padding of the last round
   } else {
-    s = x % max_split;
-    x /= max_split;
-    hk = x % p.hkv;
-    r = x / p.hkv;
+    x = divmod_u(x, max_split, s);
+    r = divmod_u(x, p.hkv, hk);
     if (r >= p.batch) return;  // padding of the last round
   }
   int n_split = cg < p.n_cg_full ? p.n_split : p.n_split_tail;
@@ -349,8 +363,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   // ---- this lane's column
   const int col = col0 + wid * kColsPerWave + n;
   const bool valid = col < ncols;
-  const int qi = valid ? col / g : 0;
-  const int head = hk * g + (valid ? col % g : 0);
+  int col_h;
+  const int col_q = divmod_u(col, g, col_h);
+  const int qi = valid ? col_q : 0;
+  const int head = hk * g + (valid ? col_h : 0);
   const uint64_t* mrow =
       has_mask ? p.mask + ((int64_t)r * p.n_q_max + qi) * p.mask_words : nullptr;
   const bool lane_mask = has_mask && valid;
@@ -684,8 +700,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     rv[rr / kRpi] =
         *(const LDS_AS u32x4*)(uintptr_t)(stage + (rr + lane / kLpr) * kRowPad + chunk * 16);
   const int cfirst = col0 + wid * kColsPerWave + lane / kLpr;
-  const int q0 = cfirst / g;
-  int ho = cfirst - q0 * g;
+  int ho;
+  const int q0 = divmod_u(cfirst, g, ho);
   const int dq = kRpi / g, dh = kRpi - dq * g;
   const int64_t ostride = SPLIT ? (int64_t)p.n_split * D : (int64_t)D;  // elements per row id
   int64_t eoff = (((int64_t)r * p.n_q_max + q0) * p.hq + hk * g + ho) * ostride +
@@ -718,16 +734,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
   const int gid = blockIdx.x * (int)(blockDim.x / kTPR) + threadIdx.x / kTPR;
   const int lane = threadIdx.x % kTPR;
   if (gid >= p.batch * p.n_q_max * p.hq) return;
-  const int head = gid % p.hq;
-  const int rq = gid / p.hq;
-  const int qi = rq % p.n_q_max;
-  const int r = rq / p.n_q_max;
+  int head, qi;
+  const int rq = divmod_u(gid, p.hq, head);
+  const int r = divmod_u(rq, p.n_q_max, qi);
   const int nq = min(p.n_q[r], p.n_q_max);
   if (qi >= nq) return;
   const int T = p.prefix_len[r] + nq;
   if (T <= 0) return;
   const int g = p.hq / p.hkv;
-  const int col = qi * g + head % g;
+  int head_in;
+  (void)divmod_u(head, g, head_in);
+  const int col = qi * g + head_in;
   const int ntiles = (T + kKT - 1) / kKT;
   const int ns = request_splits(col / kColsPerWG < p.n_cg_full ? p.n_split : p.n_split_tail,
                                 ntiles, p.max_tiles);
