@@ -431,10 +431,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     }
   };
 
-  // Q, then the split's first two tiles, are put in flight before the tile
-  // list is built.  Prefix tiles are always processed; a range that starts
-  // in the own rows is copied speculatively and re-copied below in the rare
-  // case that the list skips one of those tiles.
+  // Q, then the split's first tile, are put in flight before the tile list
+  // is built.  Prefix tiles are always processed; a range that starts in the
+  // own rows is copied speculatively and re-copied below in the rare case
+  // that the list skips that tile.
   bf16x8 qf[D / 16];
   {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(
@@ -443,9 +443,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     for (int t = 0; t < D / 16; ++t) qf[t] = qp[2 * t];
   }
   __builtin_amdgcn_sched_barrier(0);  // the Q loads stay ahead of the tile copies
-  const int n_spec = min(2, t_end - t_begin);
   issue_tile(t_begin, 0);
-  if (n_spec > 1) issue_tile(t_begin + 1, 1);
 
   // ---- tiles to process: every tile holding prefix keys, and the own-row
   // tiles in which some column of the workgroup sees a key.  The visibility
@@ -525,27 +523,27 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
 
-  // prologue: if the list does not start with the speculated tiles, let
-  // those copies land and copy the right ones.  Then Q and tile 0 are
-  // waited for.  (The compiler, which cannot order the Q loads against the
-  // LDS-direct copies, waits for every copy before the first use of Q, so
-  // tile 1 has landed too; inside the loop the only memory operations in
-  // flight are tile copies, so "all but the newest tile" is a plain vmcnt.)
-  if ((ntl > 0 && tile_at(0) != t_begin) || (ntl > 1 && n_spec > 1 && tile_at(1) != t_begin + 1) ||
-      (ntl > 1 && n_spec < 2)) {
+  // prologue: if the list does not start with the speculated tile, let
+  // that copy land and copy the right one.  Then Q and tile 0 are waited
+  // for, and only then is tile 1 copied: the compiler, which cannot order
+  // the Q loads against the LDS-direct copies, waits for every copy in
+  // flight before the first use of Q, and each CU takes its Q rows and
+  // tiles at 64 B per clock, so a tile 1 issued earlier would delay the
+  // first tile by its own transfer.  Inside the loop the only memory
+  // operations in flight are tile copies, so "all but the newest tile" is
+  // a plain vmcnt.
+  if (ntl > 0 && tile_at(0) != t_begin) {
     wait_vm<0>();
-    __builtin_amdgcn_s_barrier();  // every wave's speculative copies have landed
+    __builtin_amdgcn_s_barrier();  // every wave's speculative copy has landed
     __asm__ volatile("" ::: "memory");
-    if (ntl > 0) issue_tile(tile_at(0), 0);
-    if (ntl > 1) issue_tile(tile_at(1), 1);
+    issue_tile(tile_at(0), 0);
   }
-  if (ntl > 1) wait_vm<G::kLoads>();
-  else wait_vm<0>();
-  // Q was issued before every tile copy, so it has landed; columns past the
-  // end (loaded from row 0 of the request) are zeroed
+  wait_vm<0>();
+  // columns past the end (loaded from row 0 of the request) are zeroed
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
     if (!valid) qf[t] = bf16x8{};
+  if (ntl > 1) issue_tile(tile_at(1), 1);
 
   for (int i = 0; i < ntl; ++i) {
     // this tile's copies done (the next tile's may stay in flight), then
