@@ -435,12 +435,18 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   // is built.  Prefix tiles are always processed; a range that starts in the
   // own rows is copied speculatively and re-copied below in the rare case
   // that the list skips that tile.
+  // (waves without a column of the request load no Q: in a drafter block six
+  // of the eight waves are idle, and their Q rows would take the CU's fill
+  // bandwidth ahead of the first tile)
   bf16x8 qf[D / 16];
-  {
+  if (wave_active) {
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(
         p.q + (((int64_t)r * p.n_q_max + qi) * p.hq + head) * D + 8 * h2);
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) qf[t] = qp[2 * t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) qf[t] = bf16x8{};
   }
   __builtin_amdgcn_sched_barrier(0);  // the Q loads stay ahead of the tile copies
   issue_tile(t_begin, 0);
