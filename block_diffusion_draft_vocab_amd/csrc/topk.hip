@@ -62,8 +62,20 @@ __device__ __forceinline__ int rank_among(const uint64_t* cand, int n, uint64_t 
   return rank;
 }
 
+// The k-th largest of the wave's values (one per lane, 0 meaning none), or 0
+// when fewer than k lanes hold one: the largest t with at least k lanes
+// holding v >= t, built from the top bit down, one ballot per bit.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k) {
+  uint32_t t = 0u;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    if (__popcll(__ballot(v >= c)) >= k) t = c;
+  }
+  return t;
+}
+
 struct PartialSmem {
-  uint32_t lanemax[kTopkThreads];  // order-mapped thread maxima
   float wmax[kWaves];
   float wsum[kWaves];
   uint32_t thr[kWaves];
@@ -130,7 +142,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
 #pragma unroll
   for (int i = 0; i < PER; ++i) tm = fmaxf(tm, x[i]);
   const float wm = wave_max_f(tm);
-  sm.lanemax[tid] = f32_order(tm);
   if (lane == 0) sm.wmax[wid] = wm;
   if (tid == 0) sm.cand_n = 0;
   __syncthreads();
@@ -139,9 +150,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
   const float M = fmaxf(fmaxf(sm.wmax[0], sm.wmax[1]), fmaxf(sm.wmax[2], sm.wmax[3]));
   float s = 0.f;
   if (M != -INFINITY) {
+    // four running sums, so the exponentials do not wait on one add chain
     const float mb = M * kLog2e;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < PER; ++i) s += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mb));
+    for (int i = 0; i < PER; ++i) s4[i & 3] += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mb));
+    s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   }
   const float ws = wave_sum_f(s);
   if (lane == 0) sm.wsum[wid] = ws;
@@ -156,17 +170,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     const int nw = (lanes + kWave - 1) / kWave;
     const int kw = (k + nw - 1) / nw;
     const bool me_valid = tm != -INFINITY;
-    const uint32_t me = me_valid ? sm.lanemax[tid] : 0u;
-    const uint4* lm4 = reinterpret_cast<const uint4*>(sm.lanemax + wid * kWave);
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kWave / 4; ++j) {
-      const uint4 q = lm4[j];
-      cnt += (q.x >= me) + (q.y >= me) + (q.z >= me) + (q.w >= me);
-    }
-    // invalid lanes hold f32_order(-inf) > 0 in lanemax; they are never
-    // >= a valid lane's value, so cnt of a valid lane counts valid lanes only
-    const uint32_t t = wave_max_u32(me_valid && cnt >= kw ? me : 0u);
+    // a valid lane's order-mapped maximum is above f32_order(-inf) > 0, so 0
+    // marks the lanes without a key
+    const uint32_t t = wave_kth_largest(me_valid ? f32_order(tm) : 0u, kw);
     const uint64_t any_valid = __ballot(me_valid);
     if (lane == 0) sm.thr[wid] = any_valid == 0 ? 0xFFFFFFFFu : t;
   }
