@@ -134,17 +134,6 @@ __device__ __forceinline__ int request_splits(int ns, int nt, int max_tiles) {
                      : ((long)nt * ns + max_tiles - 1) / max_tiles;
   return v < 1 ? 1 : (v > ns ? ns : (int)v);
 }
-// x / d and x % d for x >= 0 and d > 0 uniform: a shift and a mask when d is
-// a power of two (the usual q-heads per KV head), else the division.
-__device__ __forceinline__ int divmod_u(int x, int d, int& rem) {
-  if ((d & (d - 1)) == 0) {
-    rem = x & (d - 1);
-    return x >> __builtin_ctz((unsigned)d);
-  }
-  const int q = (int)((unsigned)x / (unsigned)d);
-  rem = x - q * d;
-  return q;
-}
 // Split s is empty only when there are fewer tiles than splits.
 __device__ __forceinline__ bool split_nonempty(int s, int n_split, int nt) {
   if (nt >= n_split) return true;

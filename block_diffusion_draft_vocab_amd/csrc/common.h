@@ -21,6 +21,30 @@ __device__ __forceinline__ float f32_unorder(uint32_t o) {
   return __uint_as_float(b);
 }
 
+// x / d and x % d for x >= 0 and d > 0 the same across the wave: a shift
+// and a mask when d is a power of two (the usual head-group sizes and
+// top-K widths), else the division.
+__device__ __forceinline__ int divmod_u(int x, int d, int& rem) {
+  if ((d & (d - 1)) == 0) {
+    rem = x & (d - 1);
+    return x >> __builtin_ctz((unsigned)d);
+  }
+  const int q = (int)((unsigned)x / (unsigned)d);
+  rem = x - q * d;
+  return q;
+}
+
+// floor(a / b) for 0 <= a < 2^21 and b >= 1 (b may differ across lanes):
+// the float estimate from the reciprocal is within one of the quotient
+// (relative error below 2^-22), and one correction step either way makes
+// it exact.
+__device__ __forceinline__ int div_small(int a, int b) {
+  int q = (int)((float)a * __builtin_amdgcn_rcpf((float)b));
+  if (q * b > a) --q;
+  else if ((q + 1) * b <= a) ++q;
+  return q;
+}
+
 // 16-byte streaming load (non-temporal hint: the line is not kept for
 // reuse), for data read exactly once such as a pass over the logits.
 __device__ __forceinline__ float4 load_f4_stream(const float* p) {

@@ -130,8 +130,8 @@ __global__ __launch_bounds__(1024) void tree_kernel(
   const int W = (n_max + 63) / 64;
 
   for (int i = tid; i < L * k_tree; i += nt) {
-    const int d = i / k_tree;
-    const int rk = i - d * k_tree;
+    int rk;
+    const int d = divmod_u(i, k_tree, rk);
     y[i] = logp[((int64_t)r * L + d) * K + rk];
   }
   // gb: G (sorted, g keys) with the level's children appended after it;
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       // min(k_tree, B / (j + 1)) children and the run offsets are one wave
       // scan, done by every wave alike: no search, no barrier.  The shuffles
       // run with every lane active (a uniform trip count).
-      const int lenj = lane < n ? min(k_tree, B / (lane + 1)) : 0;
+      const int lenj = lane < n ? min(k_tree, div_small(B, lane + 1)) : 0;
       const int incj = wave_inclusive_scan(lenj);
       nc = __builtin_amdgcn_readlane(incj, kWave - 1);
       if (nc == 0) break;
@@ -205,8 +205,9 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       const int items = n * k_tree;
       for (int base = 0; base < items; base += nt) {
         const int it = base + tid;
-        const int j = it < items ? it / k_tree : 0;
-        const int c = it - j * k_tree;
+        int c;
+        int j = divmod_u(it, k_tree, c);
+        if (it >= items) j = c = 0;
         const int len = __shfl(lenj, j, kWave);
         const int o = __shfl(exj, j, kWave);
         const float ps = __shfl(psj, j, kWave);
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(1024) void tree_kernel(
         const int j = tid * per + u;
         int len = 0;
         if (u < per && j < n) {
-          int lo = 0, hi = min(k_tree, B / (j + 1));
+          int lo = 0, hi = min(k_tree, div_small(B, j + 1));
           float ps;
           if (d == 2) {
             ps = 0.0f + y[j];  // the key of G[j], exactly
@@ -271,8 +272,8 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       // children keys after G: run 0 = G at [0, g), run j+1 = parent j's
       const int items = n * k_tree;
       for (int it = tid; it < items; it += nt) {
-        const int j = it / k_tree;
-        const int c = it - j * k_tree;
+        int c;
+        const int j = divmod_u(it, k_tree, c);
         const int o = rcnt[j];
         const int len = (j + 1 < n ? rcnt[j + 1] : nc) - o;
         if (c < len) gb[g + o + c] = tkey(pscore[j] + yd[c], d, j, c);
