@@ -106,7 +106,15 @@ struct Params {
   int max_tiles;      // key tiles of the longest request the plan was made for
   int block_len;      // > 0: own rows form blocks of this many rows, each query
                       // sees only its own block's rows (packed drafter blocks)
+  int g;              // q-heads per KV head
   float scale_log2;
+  // the launch's fixed divisors, as multiply-and-shift pairs
+  FastDiv fd_groups;  // column groups per (request, KV head, split)
+  FastDiv fd_msplit;  // max(n_split, n_split_tail)
+  FastDiv fd_hkv, fd_hq, fd_g, fd_nq_max;
+  FastDiv fd_tiles;   // max_tiles
+  FastDiv fd_split, fd_split_tail;
+  FastDiv fd_block;   // block_len (1 without packed blocks)
 };
 
 // Tiles [t0, t1) of split s out of n_split over nt tiles (balanced; 32-bit
@@ -114,8 +122,14 @@ struct Params {
 // Tiles [t0, t1) of split s: nt / n_split each, the remainder one apiece to
 // the first splits.  Those are dispatched first, and the last split, which
 // holds the own rows (and their visibility setup), stays among the short ones.
-__device__ __forceinline__ void split_range(int s, int n_split, int nt, int& t0, int& t1) {
-  const int q = nt / n_split;
+__device__ __forceinline__ void split_range(int s, int n_split, int nt, int& t0, int& t1,
+                                            const Params& p) {
+  // the plan's split counts divide through their multipliers; a count
+  // scaled down for a shorter request through the float estimate
+  const int q = n_split == (int)p.fd_split.d         ? fdiv(nt, p.fd_split)
+                : n_split == (int)p.fd_split_tail.d  ? fdiv(nt, p.fd_split_tail)
+                : nt < (1 << 21)                     ? div_small(nt, n_split)
+                                                     : (int)((unsigned)nt / (unsigned)n_split);
   const int rem = nt - q * n_split;
   t0 = s * q + (s < rem ? s : rem);
   t1 = t0 + q + (s < rem ? 1 : 0);
@@ -124,21 +138,20 @@ __device__ __forceinline__ void split_range(int s, int n_split, int nt, int& t0,
 // request's share of the longest key range, so that a short request in a
 // ragged batch gets splits of about the same length as the longest one
 // (never more tiles per split than the plan allows: ns >= max_tiles / 16).
-__device__ __forceinline__ int request_splits(int ns, int nt, int max_tiles) {
+__device__ __forceinline__ int request_splits(int ns, int nt, const Params& p) {
+  const int max_tiles = p.max_tiles;
   if (nt >= max_tiles) return ns;
-  // 32-bit arithmetic whenever the product fits (a 64-bit division is a long
-  // instruction sequence at the head of every workgroup)
-  const long v = max_tiles <= 0xFFFF
-                     ? (long)(((uint32_t)nt * (uint32_t)ns + (uint32_t)max_tiles - 1u) /
-                              (uint32_t)max_tiles)
-                     : ((long)nt * ns + max_tiles - 1) / max_tiles;
+  // below 2^16 tiles the plan keeps ns <= 4096, so the rounded-up product
+  // stays under 2^31 and divides through the multiplier
+  const long v = max_tiles <= 0xFFFF ? (long)fdiv(nt * ns + max_tiles - 1, p.fd_tiles)
+                                     : ((long)nt * ns + max_tiles - 1) / max_tiles;
   return v < 1 ? 1 : (v > ns ? ns : (int)v);
 }
 // Split s is empty only when there are fewer tiles than splits.
-__device__ __forceinline__ bool split_nonempty(int s, int n_split, int nt) {
+__device__ __forceinline__ bool split_nonempty(int s, int n_split, int nt, const Params& p) {
   if (nt >= n_split) return true;
   int t0, t1;
-  split_range(s, n_split, nt, t0, t1);
+  split_range(s, n_split, nt, t0, t1, p);
   return t0 < t1;
 }
 
@@ -283,7 +296,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   asm volatile("" ::"s"(p.mask), "s"(p.out), "s"(p.lse), "s"(p.part_o), "s"(p.part_ml));
   asm volatile("" ::"s"(p.batch), "s"(p.hq), "s"(p.hkv), "s"(p.n_q_max), "s"(p.mask_words),
                "s"(p.n_cg_full), "s"(p.n_split), "s"(p.n_split_tail), "s"(p.max_tiles),
-               "s"(p.block_len), "s"(p.scale_log2));
+               "s"(p.block_len), "s"(p.g), "s"(p.scale_log2));
+  asm volatile("" ::"s"(p.fd_groups.m), "s"(p.fd_groups.s), "s"(p.fd_msplit.m),
+               "s"(p.fd_msplit.s), "s"(p.fd_hkv.m), "s"(p.fd_hkv.s), "s"(p.fd_g.m), "s"(p.fd_g.s),
+               "s"(p.fd_tiles.m), "s"(p.fd_tiles.s), "s"(p.fd_split.m), "s"(p.fd_split.s));
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem_raw[];
   __shared__ int tile_list[kMaxTilesPerSplit];
   __shared__ int n_tiles_s;
@@ -307,20 +323,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   // Several requests: split fastest, so the splits of one request land on
   // different XCDs and every XCD gets a similar mix of long and short
   // requests (ragged serving batch 327 -> 303 us per step stage).
-  const int n_groups = p.n_cg_full + (p.n_split_tail > 0 ? 1 : 0);
   const int max_split = p.n_split > p.n_split_tail ? p.n_split : p.n_split_tail;
   const int xcd = blockIdx.x % kXcds;
   const int jx = blockIdx.x / kXcds;
   int cg;
-  int x = divmod_u(jx, n_groups, cg) * kXcds + xcd;
+  int x = fdivmod(jx, p.fd_groups, cg) * kXcds + xcd;
   int s, hk, r;
   if (p.batch == 1) {
     r = 0;
-    s = divmod_u(x, p.hkv, hk);
+    s = fdivmod(x, p.fd_hkv, hk);
     if (s >= max_split) return;  // padding of the last round
   } else {
-    x = divmod_u(x, max_split, s);
-    r = divmod_u(x, p.hkv, hk);
+    x = fdivmod(x, p.fd_msplit, s);
+    r = fdivmod(x, p.fd_hkv, hk);
     if (r >= p.batch) return;  // padding of the last round
   }
   int n_split = cg < p.n_cg_full ? p.n_split : p.n_split_tail;
@@ -332,15 +347,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   asm volatile("" ::"s"(P), "s"(nq_req), "s"(base));
   const int nq = min(nq_req, p.n_q_max);
   const int T = P + nq;
-  const int g = p.hq / p.hkv;
+  const int g = p.g;
   const int ncols = nq * g;
   const int col0 = cg * kColsPerWG;
   if (col0 >= ncols || T <= 0) return;
   const int ntiles = (T + kKT - 1) / kKT;
-  n_split = request_splits(n_split, ntiles, p.max_tiles);
+  n_split = request_splits(n_split, ntiles, p);
   if (s >= n_split) return;
   int t_begin, t_end;
-  split_range(s, n_split, ntiles, t_begin, t_end);
+  split_range(s, n_split, ntiles, t_begin, t_end, p);
   if (t_begin >= t_end) return;
   // a split spans at most kMaxTilesPerSplit tiles whenever every request's
   // prefix_len + n_q is within the max_kv_len the plan was made for; the
@@ -353,14 +368,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   const int col = col0 + wid * kColsPerWave + n;
   const bool valid = col < ncols;
   int col_h;
-  const int col_q = divmod_u(col, g, col_h);
+  const int col_q = fdivmod(col, p.fd_g, col_h);
   const int qi = valid ? col_q : 0;
   const int head = hk * g + (valid ? col_h : 0);
   const uint64_t* mrow =
       has_mask ? p.mask + ((int64_t)r * p.n_q_max + qi) * p.mask_words : nullptr;
   const bool lane_mask = has_mask && valid;
   // own rows this column may see: all nq, or its packed block
-  const int own_lo = p.block_len > 0 ? (qi / p.block_len) * p.block_len : 0;
+  const int own_lo = p.block_len > 0 ? fdiv(qi, p.fd_block) * p.block_len : 0;
   const int own_hi = p.block_len > 0 ? min(nq, own_lo + p.block_len) : nq;
 
   // ---- staging: copy j of this thread moves 16-byte chunk
@@ -694,8 +709,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
         *(const LDS_AS u32x4*)(uintptr_t)(stage + (rr + lane / kLpr) * kRowPad + chunk * 16);
   const int cfirst = col0 + wid * kColsPerWave + lane / kLpr;
   int ho;
-  const int q0 = divmod_u(cfirst, g, ho);
-  const int dq = kRpi / g, dh = kRpi - dq * g;
+  const int q0 = fdivmod(cfirst, p.fd_g, ho);
+  const int dq = fdiv(kRpi, p.fd_g), dh = kRpi - dq * g;
   const int64_t ostride = SPLIT ? (int64_t)p.n_split * D : (int64_t)D;  // elements per row id
   int64_t eoff = (((int64_t)r * p.n_q_max + q0) * p.hq + hk * g + ho) * ostride +
                  (SPLIT ? (int64_t)s * D : 0) + chunk * 8;
@@ -728,19 +743,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
   const int lane = threadIdx.x % kTPR;
   if (gid >= p.batch * p.n_q_max * p.hq) return;
   int head, qi;
-  const int rq = divmod_u(gid, p.hq, head);
-  const int r = divmod_u(rq, p.n_q_max, qi);
+  const int rq = fdivmod(gid, p.fd_hq, head);
+  const int r = fdivmod(rq, p.fd_nq_max, qi);
   const int nq = min(p.n_q[r], p.n_q_max);
   if (qi >= nq) return;
   const int T = p.prefix_len[r] + nq;
   if (T <= 0) return;
-  const int g = p.hq / p.hkv;
+  const int g = p.g;
   int head_in;
-  (void)divmod_u(head, g, head_in);
+  (void)fdivmod(head, p.fd_g, head_in);
   const int col = qi * g + head_in;
   const int ntiles = (T + kKT - 1) / kKT;
   const int ns = request_splits(col / kColsPerWG < p.n_cg_full ? p.n_split : p.n_split_tail,
-                                ntiles, p.max_tiles);
+                                ntiles, p);
   const int64_t ro = (int64_t)gid * p.n_split;
   float M = -INFINITY;
   float Lsum = 0.f;
@@ -751,7 +766,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int sp = sp0 + u;
-      const bool ok = sp < ns && split_nonempty(sp, ns, ntiles);
+      const bool ok = sp < ns && split_nonempty(sp, ns, ntiles, p);
       ml[u] = ok ? p.part_ml[ro + sp] : make_float2(-INFINITY, 0.f);
       raw[u] = ok ? *reinterpret_cast<const u32x4*>(p.part_o + (ro + sp) * D + lane * 8)
                   : u32x4{0u, 0u, 0u, 0u};
@@ -913,7 +928,18 @@ hipError_t launch_attention(int batch, int hq, int hkv, int head_dim, int n_q_ma
   prm.n_split_tail = plan.n_split_tail;
   prm.block_len = block_len;
   prm.max_tiles = (max_kv_len + kKT - 1) / kKT;
+  prm.g = hq / hkv;
   prm.scale_log2 = scale * kLog2e;
+  prm.fd_groups = make_fastdiv(plan.n_cg_full + (plan.n_split_tail > 0 ? 1 : 0));
+  prm.fd_msplit = make_fastdiv(plan.n_split > plan.n_split_tail ? plan.n_split : plan.n_split_tail);
+  prm.fd_hkv = make_fastdiv(hkv);
+  prm.fd_hq = make_fastdiv(hq);
+  prm.fd_g = make_fastdiv(hq / hkv);
+  prm.fd_nq_max = make_fastdiv(n_q_max);
+  prm.fd_tiles = make_fastdiv(prm.max_tiles);
+  prm.fd_split = make_fastdiv(plan.n_split);
+  prm.fd_split_tail = make_fastdiv(plan.n_split_tail);
+  prm.fd_block = make_fastdiv(block_len > 0 ? block_len : 1);
   switch (head_dim) {
     case 32: return launch_d<32>(prm, plan, stream);
     case 64: return launch_d<64>(prm, plan, stream);

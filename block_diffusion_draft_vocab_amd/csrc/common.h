@@ -34,6 +34,38 @@ __device__ __forceinline__ int divmod_u(int x, int d, int& rem) {
   return q;
 }
 
+// Division by a divisor d >= 1 fixed for a launch, of any n in [0, 2^31):
+// with l = ceil(log2 d), m = ceil(2^(31+l) / d) fits 32 bits, and
+// n m / 2^(31+l) exceeds n / d by n e / (d 2^(31+l)) with e = m d - 2^(31+l)
+// < d <= 2^l, which stays below 1/d, so the floor is the quotient
+// (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).  The host computes (m, s); a uniform quotient is
+// then a scalar multiply and shift, a per-lane one three vector operations,
+// instead of the ~30-instruction reciprocal sequence of a runtime division.
+struct FastDiv {
+  uint32_t m;
+  uint32_t s;
+  uint32_t d;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  if (d == 0) d = 1;  // (unused divisors: any valid value)
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  FastDiv f;
+  f.s = 31 + l;
+  f.m = (uint32_t)(((1ull << f.s) + d - 1) / d);
+  f.d = d;
+  return f;
+}
+__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
+  return (int)(((uint64_t)(uint32_t)n * f.m) >> f.s);
+}
+__device__ __forceinline__ int fdivmod(int n, const FastDiv& f, int& rem) {
+  const int q = fdiv(n, f);
+  rem = n - q * (int)f.d;
+  return q;
+}
+
 // floor(a / b) for 0 <= a < 2^21 and b >= 1 (b may differ across lanes):
 // the float estimate from the reciprocal is within one of the quotient
 // (relative error below 2^-22), and one correction step either way makes
