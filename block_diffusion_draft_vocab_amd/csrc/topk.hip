@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     const int len = c1 - c0;
     const int lanes = min(kTopkThreads, (len + 3) / 4);
     const int nw = (lanes + kWave - 1) / kWave;
-    const int kw = (k + nw - 1) / nw;
+    const int kw = div_small(k + nw - 1, nw);  // (1 <= nw <= 4: no integer division)
     const bool me_valid = tm != -INFINITY;
     // a valid lane's order-mapped maximum is above f32_order(-inf) > 0, so 0
     // marks the lanes without a key
@@ -304,9 +304,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
   // keys, all distinct; mm is raised while the candidates fit 64, which
   // tightens T), so at least k keys of the row are >= T.  Chunk
   // lists shorter than k end in 0 keys, which are never >= T.
-  const int mm = max((k + n_chunks - 1) / n_chunks, min(k, kWave / n_chunks));
+  const int mm = max(div_small(k + n_chunks - 1, n_chunks), min(k, div_small(kWave, n_chunks)));
   const int ns = n_chunks * mm;  // <= max(k + n_chunks, 64) <= 256
-  if (tid < ns) sm.cand[tid] = lk[(tid / mm) * k + (tid % mm)];
+  if (tid < ns) {
+    const int li = div_small(tid, mm);
+    sm.cand[tid] = lk[li * k + (tid - li * mm)];
+  }
   __syncthreads();
   if (tid < ns) {
     const uint64_t v = sm.cand[tid];
@@ -430,7 +433,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
   // candidates: the first mm keys of every list, as many as fit C per
   // lane (a larger set gives a tighter T and fewer keys to rank), at least
   // ceil(k / n_chunks) so that at least k candidates exist
-  const int mm = max((k + n_chunks - 1) / n_chunks, min(k, C * kWave / n_chunks));
+  const int mm = max(div_small(k + n_chunks - 1, n_chunks), min(k, div_small(C * kWave, n_chunks)));
   const int ns = n_chunks * mm;  // <= 64 C (host check)
 
   // all global loads first: keys, threshold candidates, chunk (max, sum)
@@ -458,7 +461,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
 #pragma unroll
   for (int q = 0; q < C; ++q) {
     const int ci = lane + q * kWave;
-    c[q] = lists[ci < ns ? (ci / mm) * k + ci % mm : 0];
+    const int li = div_small(ci, mm);  // (float quotient: ci < 128)
+    c[q] = lists[ci < ns ? li * k + (ci - li * mm) : 0];
   }
   const float2* ms = part_ms + (int64_t)row * n_chunks;
   const float2 p0 = ms[lane < n_chunks ? lane : 0];
