@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
   const int nch = row_elems / 8;  // 16-byte segments per row
   const int64_t row0 = kv_base[r] + P;
   const int per_round = kAcceptThreads * kRegs;
-  int cols = per_round / (2 * len);
+  int cols = div_small(per_round, 2 * len);
   cols = cols < 1 ? 1 : cols;
   for (int c0 = 0; c0 < nch; c0 += cols) {
     const int cw = min(cols, nch - c0);
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
     // j's destination row P + j can only be the source of an earlier entry
     // (path slots increase along the path and path[j] >= j), which an
     // earlier round (or the gather before this round's barrier) has read.
-    const int jb = max(1, per_round / (2 * cw));
+    const int jb = max(1, div_small(per_round, 2 * cw));
     for (int j0 = 1; j0 <= len; j0 += jb) {
       const int nj = min(jb, len - j0 + 1);
       const int per_tensor = nj * cw;
@@ -99,10 +99,13 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
       for (int i = 0; i < kRegs; ++i) {
         const int it = tid + i * kAcceptThreads;
         if (it < items) {
-          const int tsel = it / per_tensor;
+          // (items = 2 per_tensor: the tensor is one compare; rem < 2^11,
+          // so the float quotient is exact)
+          const int tsel = it >= per_tensor ? 1 : 0;
           const int rem = it - tsel * per_tensor;
-          const int j = j0 + rem / cw;
-          const int c = c0 + rem % cw;
+          const int q = div_small(rem, cw);
+          const int j = j0 + q;
+          const int c = c0 + rem - q * cw;
           const uint16_t* base = (tsel == 0 ? k_cache : v_cache) + layer * layer_stride;
           regs[i] = *reinterpret_cast<const u32x4*>(base + (row0 + path[j]) * row_elems + c * 8);
         }
@@ -112,10 +115,11 @@ __global__ __launch_bounds__(kAcceptThreads) void accept_kernel(
       for (int i = 0; i < kRegs; ++i) {
         const int it = tid + i * kAcceptThreads;
         if (it < items) {
-          const int tsel = it / per_tensor;
+          const int tsel = it >= per_tensor ? 1 : 0;
           const int rem = it - tsel * per_tensor;
-          const int j = j0 + rem / cw;
-          const int c = c0 + rem % cw;
+          const int q = div_small(rem, cw);
+          const int j = j0 + q;
+          const int c = c0 + rem - q * cw;
           if (path[j] != j) {
             uint16_t* base = (tsel == 0 ? k_cache : v_cache) + layer * layer_stride;
             *reinterpret_cast<u32x4*>(base + (row0 + j) * row_elems + c * 8) = regs[i];
