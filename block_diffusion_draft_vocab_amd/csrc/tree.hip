@@ -124,6 +124,7 @@ __global__ __launch_bounds__(1024) void tree_kernel(
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int nt = blockDim.x;
+  const int nt_log = __builtin_ctz((unsigned)nt);  // the launch gives 256, 512 or 1024 threads
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
   const int n_max = B + 1;
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       // (j+1)(c+1) <= B; keys fall with c, so a binary search finds it.
       // Thread t owns parents [t*per, t*per + per).
       // (n <= B < 2 * nt: the launch gives max(cand_cap, 1024) threads or more)
-      const int per = (n + nt - 1) / nt;
+      const int per = (n + nt - 1) >> nt_log;
       int lens[2] = {0, 0};
       int mine = 0;
 #pragma unroll
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       smax = wave_max_f(smax);
       smin = -wave_max_f(-smin);
       const float bscale = smax > smin ? (float)(kBuckets - 1) / (smax - smin) : 0.f;
-      const int M = (total + nt - 1) / nt;  // slots in use (uniform)
+      const int M = (total + nt - 1) >> nt_log;  // slots in use (uniform)
       uint64_t xk[kMaxCarry];
       int xb[kMaxCarry], xs[kMaxCarry];
 #pragma unroll
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(1024) void tree_kernel(
       // nwaves buckets (rows of 64, read coalesced) into prefixes within the
       // segment and leaves the segment's total; a bucket's start is that
       // prefix plus the totals of the segments before it
-      const int seg = kBuckets / nwaves;  // nwaves <= 16: 1024 threads at most
+      const int seg = kBuckets >> (nt_log - 6);  // kBuckets / nwaves (nwaves <= 16)
       {
         int run = 0;
         for (int r0 = 0; r0 < seg; r0 += kWave) {
