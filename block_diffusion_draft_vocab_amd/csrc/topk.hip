@@ -62,13 +62,18 @@ __device__ __forceinline__ int rank_among(const uint64_t* cand, int n, uint64_t 
   return rank;
 }
 
-// The k-th largest of the wave's values (one per lane, 0 meaning none), or 0
-// when fewer than k lanes hold one: the largest t with at least k lanes
-// holding v >= t, built from the top bit down, one ballot per bit.
-__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k) {
+// A lower bound on the k-th largest of the wave's values (one per lane, 0
+// meaning none), or 0 when fewer than k lanes hold one: the largest t whose
+// low 16 bits are zero with at least k lanes holding v >= t, built from the
+// top bit down, one ballot per bit.  That is the k-th largest with its low
+// 16 bits cleared (the lane count above a bound only grows as the bound
+// falls), so at least k lanes still reach it; for order-mapped floats it
+// sits within 2^-7 of the value, and half the rounds of the exact search
+// are saved.
+__device__ __forceinline__ uint32_t wave_kth_largest_hi16(uint32_t v, int k) {
   uint32_t t = 0u;
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= 16; --b) {
     const uint32_t c = t | (1u << b);
     if (__popcll(__ballot(v >= c)) >= k) t = c;
   }
@@ -161,7 +166,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
   if (lane == 0) sm.wsum[wid] = ws;
   // Per-wave threshold.  With nw non-empty waves and kw = ceil(k / nw):
   // a wave with >= kw valid lanes takes T_w = its kw-th largest lane
-  // maximum (>= kw of its keys are >= T_w); a wave with fewer valid lanes
+  // maximum, rounded down to 16 significant bits (>= kw of its keys are
+  // >= T_w); a wave with fewer valid lanes
   // takes T_w = 0 (all its keys); an empty wave does not vote.  Then
   // T = min T_w leaves at least k keys (or all of them) >= T.
   {
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     const bool me_valid = tm != -INFINITY;
     // a valid lane's order-mapped maximum is above f32_order(-inf) > 0, so 0
     // marks the lanes without a key
-    const uint32_t t = wave_kth_largest(me_valid ? f32_order(tm) : 0u, kw);
+    const uint32_t t = wave_kth_largest_hi16(me_valid ? f32_order(tm) : 0u, kw);
     const uint64_t any_valid = __ballot(me_valid);
     if (lane == 0) sm.thr[wid] = any_valid == 0 ? 0xFFFFFFFFu : t;
   }
