@@ -57,10 +57,10 @@ inline FastDiv make_fastdiv(uint32_t d) {
   f.d = d;
   return f;
 }
-__device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
+__host__ __device__ __forceinline__ int fdiv(int n, const FastDiv& f) {
   return (int)(((uint64_t)(uint32_t)n * f.m) >> f.s);
 }
-__device__ __forceinline__ int fdivmod(int n, const FastDiv& f, int& rem) {
+__host__ __device__ __forceinline__ int fdivmod(int n, const FastDiv& f, int& rem) {
   const int q = fdiv(n, f);
   rem = n - q * (int)f.d;
   return q;
