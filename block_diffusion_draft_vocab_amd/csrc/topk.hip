@@ -417,10 +417,10 @@ constexpr int kWaveCandCap = 512;  // keys >= T a wave ranks in LDS
 // The same merge with one wave per row and no block barrier, for rows whose
 // n = n_chunks * k keys fit R per lane (n <= 64 R) and whose threshold
 // candidates fit C per lane (n_chunks * ceil(k / n_chunks) <= 64 C).  Each
-// lane holds R keys of the row in registers; the threshold T is
-// ranked among the candidates through a small LDS area of the wave; a wave
-// scan of the per-lane counts of keys >= T places those keys in LDS, and
-// each is ranked by counting the greater ones.  C = 2 serves rows where one
+// lane holds R keys of the row in registers; the threshold T comes from the
+// candidates by a ballot search on their value bits; a wave scan of the
+// per-lane counts of keys >= T places those keys in LDS, and each is ranked
+// by counting the greater ones.  C = 2 serves rows where one
 // candidate per lane would leave no more candidates than k (T would be the
 // smallest list head and let most keys through).
 template <int R, int C>
@@ -428,7 +428,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
     const uint64_t* __restrict__ part_key, const float2* __restrict__ part_ms, int n_rows,
     int n_chunks, int k, int32_t* __restrict__ ids, float* __restrict__ logp,
     float* __restrict__ lse_out) {
-  __shared__ alignas(16) uint64_t cand_all[kWaves][kWave * C];
   __shared__ alignas(16) uint64_t take_all[kWaves][kWaveCandCap];
   const int wid = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -488,28 +487,26 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
     lse = M + logf(wave_sum_f(s));
   }
 
-  // T = k-th largest candidate (0 -- take every key -- when that rank is
-  // only held by tied zero padding keys)
-  uint64_t* cw = cand_all[wid];
-  uint64_t cv[C];
+  // T = the k-th largest candidate's value part (its upper 32 bits, the
+  // order-mapped float), found from the top bit down with one ballot per
+  // candidate slot and bit: the largest t with at least k candidates whose
+  // value part is >= t.  Keys >= (t, 0) include every candidate at or above
+  // the k-th, so at least k keys; ties on the value add a few.  (0 -- take
+  // every key -- when fewer than k candidates are real keys: zero padding
+  // ends short lists.)
+  uint32_t hv[C];
 #pragma unroll
-  for (int q = 0; q < C; ++q) {
-    cv[q] = lane + q * kWave < ns ? c[q] : 0ull;
-    cw[lane + q * kWave] = cv[q];
-  }
-  wave_lds_sync();
-  uint64_t T = 0;
+  for (int q = 0; q < C; ++q) hv[q] = lane + q * kWave < ns ? (uint32_t)(c[q] >> 32) : 0u;
+  uint32_t tv = 0u;
 #pragma unroll
-  for (int q = 0; q < C; ++q) {
-    const int crank = rank_among(cw, ns, cv[q]);
-    const uint64_t hit = __ballot(lane + q * kWave < ns && crank == k - 1);
-    if (hit != 0) {
-      const int src = __builtin_ctzll(hit);
-      T = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(cv[q] >> 32), src)
-           << 32) |
-          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)cv[q], src);
-    }
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tv | (1u << b);
+    int cnt_ge = 0;
+#pragma unroll
+    for (int q = 0; q < C; ++q) cnt_ge += __popcll(__ballot(hv[q] >= cand));
+    if (cnt_ge >= k) tv = cand;
   }
+  const uint64_t T = (uint64_t)tv << 32;
 
   // this lane's keys >= T
   int cnt = 0;
