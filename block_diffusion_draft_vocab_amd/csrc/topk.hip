@@ -71,11 +71,14 @@ __device__ __forceinline__ int rank_among(const uint64_t* cand, int n, uint64_t 
 // sits within 2^-7 of the value, and half the rounds of the exact search
 // are saved.
 __device__ __forceinline__ uint32_t wave_kth_largest_hi16(uint32_t v, int k) {
+  // (v opaque to the compiler: each round's compare then feeds its ballot
+  // directly instead of being re-materialised through a select)
+  __asm__ volatile("" : "+v"(v));
   uint32_t t = 0u;
 #pragma unroll
   for (int b = 31; b >= 16; --b) {
     const uint32_t c = t | (1u << b);
-    if (__popcll(__ballot(v >= c)) >= k) t = c;
+    if (__popcll(__builtin_amdgcn_ballot_w64(v >= c)) >= k) t = c;
   }
   return t;
 }
@@ -496,14 +499,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
   // ends short lists.)
   uint32_t hv[C];
 #pragma unroll
-  for (int q = 0; q < C; ++q) hv[q] = lane + q * kWave < ns ? (uint32_t)(c[q] >> 32) : 0u;
+  for (int q = 0; q < C; ++q) {
+    hv[q] = lane + q * kWave < ns ? (uint32_t)(c[q] >> 32) : 0u;
+    // (opaque to the compiler, so every round's compare feeds its ballot
+    // directly instead of being re-materialised through a select)
+    __asm__ volatile("" : "+v"(hv[q]));
+  }
   uint32_t tv = 0u;
 #pragma unroll
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = tv | (1u << b);
     int cnt_ge = 0;
 #pragma unroll
-    for (int q = 0; q < C; ++q) cnt_ge += __popcll(__ballot(hv[q] >= cand));
+    for (int q = 0; q < C; ++q) cnt_ge += __popcll(__builtin_amdgcn_ballot_w64(hv[q] >= cand));
     if (cnt_ge >= k) tv = cand;
   }
   const uint64_t T = (uint64_t)tv << 32;
