@@ -431,7 +431,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
     const uint64_t* __restrict__ part_key, const float2* __restrict__ part_ms, int n_rows,
     int n_chunks, int k, int32_t* __restrict__ ids, float* __restrict__ logp,
     float* __restrict__ lse_out) {
-  __shared__ alignas(16) uint64_t take_all[kWaves][kWaveCandCap];
+  __shared__ alignas(16) uint64_t take_all[kWaves][kWaveCandCap + kWave];  // + a spare slot per lane
   const int wid = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int row = blockIdx.x * (int)(blockDim.x / kWave) + wid;
@@ -526,10 +526,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_merge_wave_kernel(
   float* olp = logp + (int64_t)row * k;
   if (nc <= kWaveCandCap) {
     uint64_t* tw = take_all[wid];
+    // every key is written, without a branch per key: the ones not taken
+    // go to the lane's spare slot
     int o = inc - cnt;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if ((kidx(r) < n) && key[r] >= T) tw[o++] = key[r];
+      const bool take = (kidx(r) < n) && key[r] >= T;
+      tw[take ? o : kWaveCandCap + lane] = key[r];
+      o += take ? 1 : 0;
     }
     wave_lds_sync();
     for (int t = lane; t < nc; t += kWave) {
