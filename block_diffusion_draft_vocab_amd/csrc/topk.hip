@@ -88,7 +88,7 @@ struct PartialSmem {
   float wsum[kWaves];
   uint32_t thr[kWaves];
   int cand_n;
-  alignas(16) uint64_t cand[kCandCap];
+  alignas(16) uint64_t cand[kCandCap + kWave];  // + a spare slot per lane
 };
 
 template <int PER>
@@ -214,12 +214,26 @@ __global__ __launch_bounds__(kTopkThreads) void topk_partial_kernel(
     base = __builtin_amdgcn_readfirstlane(base);
     if (holder) {
       int pos = base + incl - mine;
+      if constexpr (PER <= 20) {
+        // every element written, without a branch per element (the keys
+        // not taken, or past the cap, go to the lane's spare slot); with
+        // 32 values per thread the extra LDS writes cost more than the
+        // branches they save
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if (x[i] >= tf) {
+        for (int i = 0; i < PER; ++i) {
+          const bool take = x[i] >= tf;
           const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
-          if (pos < kCandCap) sm.cand[pos] = make_key(x[i], idx);
-          ++pos;
+          sm.cand[take && pos < kCandCap ? pos : kCandCap + lane] = make_key(x[i], idx);
+          pos += take ? 1 : 0;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          if (x[i] >= tf) {
+            const int idx = c0 + ((i >> 2) * kTopkThreads + tid) * 4 + (i & 3);
+            if (pos < kCandCap) sm.cand[pos] = make_key(x[i], idx);
+            ++pos;
+          }
         }
       }
     }
