@@ -733,43 +733,74 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 
 // Merge of the key splits: one group of D/8 threads per (request, query
 // row, q-head), each thread owning 8 consecutive output elements (16-byte
-// partial loads and stores).  Splits are read 16 at a time with all 32 loads
-// in flight, merged into a running (max, weighted sum) like the tile loop.
-template <int D>
+// partial loads and stores).  Splits are read kBatch at a time with all
+// 2 * kBatch loads in flight, merged into a running (max, weighted sum) like
+// the tile loop.  With one request (kSpec), whose length the plan was sized
+// for, the first batch is loaded before the request's sizes arrive: its slot
+// indexes are clamped to the plan's split count for the row's column group
+// (inside the row's stride, so every load is unconditional and in bounds),
+// and the slots the request leaves empty or repeats are masked once the
+// sizes are known, so the launch waits on one round trip of loads instead of
+// two.  A batch of requests of mixed lengths loads only the slots each
+// request fills.
+template <int D, int kBatch, bool kSpec>
 __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
   constexpr int kTPR = D / 8;
-  constexpr int kBatch = 16;
   const int gid = blockIdx.x * (int)(blockDim.x / kTPR) + threadIdx.x / kTPR;
   const int lane = threadIdx.x % kTPR;
   if (gid >= p.batch * p.n_q_max * p.hq) return;
   int head, qi;
   const int rq = fdivmod(gid, p.fd_hq, head);
   const int r = fdivmod(rq, p.fd_nq_max, qi);
-  const int nq = min(p.n_q[r], p.n_q_max);
-  if (qi >= nq) return;
-  const int T = p.prefix_len[r] + nq;
-  if (T <= 0) return;
   const int g = p.g;
   int head_in;
   (void)fdivmod(head, p.fd_g, head_in);
   const int col = qi * g + head_in;
-  const int ntiles = (T + kKT - 1) / kKT;
-  const int ns = request_splits(col / kColsPerWG < p.n_cg_full ? p.n_split : p.n_split_tail,
-                                ntiles, p);
+  const int ns_plan = col / kColsPerWG < p.n_cg_full ? p.n_split : p.n_split_tail;
   const int64_t ro = (int64_t)gid * p.n_split;
+  const int nq_r = p.n_q[r];
+  const int prefix_r = p.prefix_len[r];
+  float2 ml[kBatch];
+  u32x4 raw[kBatch];
+  if constexpr (kSpec) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int su = u < ns_plan ? u : (ns_plan > 0 ? ns_plan - 1 : 0);
+      ml[u] = p.part_ml[ro + su];
+      raw[u] = *reinterpret_cast<const u32x4*>(p.part_o + (ro + su) * D + lane * 8);
+    }
+    // every load above is issued before the first use of the sizes waits
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int nq = min(nq_r, p.n_q_max);
+  const int T = prefix_r + nq;
+  const bool live = qi < nq && T > 0;
+  const int ntiles = (T + kKT - 1) / kKT;
+  const int ns = live ? request_splits(ns_plan, ntiles, p) : 0;
   float M = -INFINITY;
   float Lsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int sp0 = 0; sp0 < ns; sp0 += kBatch) {
-    float2 ml[kBatch];
-    u32x4 raw[kBatch];
+    if (kSpec && sp0 == 0) {
+      // slots past the request's splits (repeats included) or left empty
+      if (ns < kBatch || ntiles < ns) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int sp = sp0 + u;
-      const bool ok = sp < ns && split_nonempty(sp, ns, ntiles, p);
-      ml[u] = ok ? p.part_ml[ro + sp] : make_float2(-INFINITY, 0.f);
-      raw[u] = ok ? *reinterpret_cast<const u32x4*>(p.part_o + (ro + sp) * D + lane * 8)
-                  : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < kBatch; ++u) {
+          if (!(u < ns && split_nonempty(u, ns, ntiles, p))) {
+            ml[u] = make_float2(-INFINITY, 0.f);
+            raw[u] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int sp = sp0 + u;
+        const bool ok = sp < ns && split_nonempty(sp, ns, ntiles, p);
+        ml[u] = ok ? p.part_ml[ro + sp] : make_float2(-INFINITY, 0.f);
+        raw[u] = ok ? *reinterpret_cast<const u32x4*>(p.part_o + (ro + sp) * D + lane * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
+      }
     }
     float bm = M;
 #pragma unroll
@@ -791,6 +822,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
       }
     }
   }
+  if (!live) return;
   const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
   u32x4 wv;
 #pragma unroll
@@ -822,8 +854,24 @@ hipError_t launch_d(const Params& prm, const AttnPlan& plan, hipStream_t stream)
     const int rows = prm.batch * prm.n_q_max * prm.hq;
     const int threads = (long)rows * (D / 8) < 256L * kCUs ? 64 : 256;
     const int rpb = threads / (D / 8);
-    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((rows + rpb - 1) / rpb), dim3(threads), 0,
-                       stream, prm);
+    // 8 slots per batch when the plan has at most 8 splits (fewer repeated
+    // or empty slots), else 16
+    const dim3 grid((rows + rpb - 1) / rpb);
+    if (prm.batch == 1) {
+      if (max_split <= 8)
+        hipLaunchKernelGGL((attn_combine_kernel<D, 8, true>), grid, dim3(threads), 0, stream,
+                           prm);
+      else
+        hipLaunchKernelGGL((attn_combine_kernel<D, 16, true>), grid, dim3(threads), 0, stream,
+                           prm);
+    } else {
+      if (max_split <= 8)
+        hipLaunchKernelGGL((attn_combine_kernel<D, 8, false>), grid, dim3(threads), 0, stream,
+                           prm);
+      else
+        hipLaunchKernelGGL((attn_combine_kernel<D, 16, false>), grid, dim3(threads), 0, stream,
+                           prm);
+    }
   } else {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_kernel<D, false>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);

@@ -191,3 +191,37 @@ def test_rows_beyond_n_q_untouched(gpu):
                          max_kv_len=74, out=out)
     torch.cuda.synchronize()
     assert torch.all(out[0, 10:] == 7.0)
+
+
+@pytest.mark.parametrize("D,hq,hkv,prefix,n_q,max_kv", [
+    (128, 32, 8, 100, 20, 4000),     # far shorter than the plan: most split slots unused
+    (128, 32, 8, 2048, 16, 2800),    # drafter-sized block, a few slots unused
+    (128, 32, 8, 0, 16, 3000),       # no prefix at all
+    (64, 8, 2, 700, 130, 5000),      # full column groups and a trailing one
+])
+@pytest.mark.parametrize("masked", [True, False], ids=["verify", "drafter"])
+def test_single_request_shorter_than_plan(gpu, D, hq, hkv, prefix, n_q, max_kv, masked):
+    """One request shorter than the max_kv_len the split plan was sized for,
+    with the workspace filled with NaN bit patterns first: split slots the
+    request never writes must not reach the merged output."""
+    seed = 11 + D + prefix + n_q
+    q, k, v, base = _rand_case(seed, 1, n_q, [n_q], [prefix], hq, hkv, D)
+    mask = None
+    if masked:
+        rng = np.random.default_rng(seed)
+        mask = _random_tree_mask(rng, n_q, n_q)[None]
+    W = 0 if mask is None else mask.shape[2]
+    nbytes = ddt.attention_workspace_size(ddt.attn_desc(1, hq, hkv, D, n_q, max_kv, W))
+    assert nbytes > 0
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=gpu)
+    out, lse = ddt.masked_attention(
+        dev_bf16(q, gpu), dev_bf16(k, gpu), dev_bf16(v, gpu),
+        torch.from_numpy(np.asarray(base, np.int64)).to(gpu),
+        torch.tensor([prefix], dtype=torch.int32, device=gpu),
+        torch.tensor([n_q], dtype=torch.int32, device=gpu),
+        None if mask is None else mask_to_dev(mask, gpu), max_kv_len=max_kv,
+        want_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    oout, olse = oracle_attn(bf16_f32(q), bf16_f32(k), bf16_f32(v), base, [prefix], [n_q], mask)
+    _compare(out.float().cpu().numpy(), lse.cpu().numpy(), oout, olse, [prefix], [n_q],
+             "single_request_short")
