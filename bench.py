@@ -730,7 +730,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "verify attention (attn_kernel<128,split> + attn_combine_kernel<128>)",
+            "kernel": "verify attention (attn_kernel<128,split> + attn_combine_kernel<128,8,spec>)",
             "achieved": round(verify_tflops, 3),
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
