@@ -736,13 +736,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 // partial loads and stores).  Splits are read kBatch at a time with all
 // 2 * kBatch loads in flight, merged into a running (max, weighted sum) like
 // the tile loop.  With one request (kSpec), whose length the plan was sized
-// for, the first batch is loaded before the request's sizes arrive: its slot
-// indexes are clamped to the plan's split count for the row's column group
-// (inside the row's stride, so every load is unconditional and in bounds),
-// and the slots the request leaves empty or repeats are masked once the
-// sizes are known, so the launch waits on one round trip of loads instead of
-// two.  A batch of requests of mixed lengths loads only the slots each
-// request fills.
+// for, and a plan of at most kBatch splits, every slot is loaded in one
+// batch before the request's sizes arrive: slot indexes are clamped to the
+// plan's split count for the row's column group (inside the row's stride, so
+// every load is unconditional and in bounds), and the slots the request
+// leaves empty or repeats are masked once the sizes are known, so the launch
+// waits on one round trip of loads instead of two.  A batch of requests of
+// mixed lengths loads only the slots each request fills, a batch at a time.
 template <int D, int kBatch, bool kSpec>
 __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
   constexpr int kTPR = D / 8;
@@ -760,52 +760,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
   const int64_t ro = (int64_t)gid * p.n_split;
   const int nq_r = p.n_q[r];
   const int prefix_r = p.prefix_len[r];
-  float2 ml[kBatch];
-  u32x4 raw[kBatch];
-  if constexpr (kSpec) {
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int su = u < ns_plan ? u : (ns_plan > 0 ? ns_plan - 1 : 0);
-      ml[u] = p.part_ml[ro + su];
-      raw[u] = *reinterpret_cast<const u32x4*>(p.part_o + (ro + su) * D + lane * 8);
-    }
-    // every load above is issued before the first use of the sizes waits
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const int nq = min(nq_r, p.n_q_max);
-  const int T = prefix_r + nq;
-  const bool live = qi < nq && T > 0;
-  const int ntiles = (T + kKT - 1) / kKT;
-  const int ns = live ? request_splits(ns_plan, ntiles, p) : 0;
   float M = -INFINITY;
   float Lsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int sp0 = 0; sp0 < ns; sp0 += kBatch) {
-    if (kSpec && sp0 == 0) {
-      // slots past the request's splits (repeats included) or left empty
-      if (ns < kBatch || ntiles < ns) {
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (!(u < ns && split_nonempty(u, ns, ntiles, p))) {
-            ml[u] = make_float2(-INFINITY, 0.f);
-            raw[u] = u32x4{0u, 0u, 0u, 0u};
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int sp = sp0 + u;
-        const bool ok = sp < ns && split_nonempty(sp, ns, ntiles, p);
-        ml[u] = ok ? p.part_ml[ro + sp] : make_float2(-INFINITY, 0.f);
-        raw[u] = ok ? *reinterpret_cast<const u32x4*>(p.part_o + (ro + sp) * D + lane * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+  // one batch of slots into the running (M, Lsum, acc)
+  auto merge = [&](const float2* ml, const u32x4* raw) {
     float bm = M;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) bm = fmaxf(bm, ml[u].x);
-    if (bm == -INFINITY) continue;
+    if (bm == -INFINITY) return;
     const float alpha = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - bm);
     Lsum *= alpha;
 #pragma unroll
@@ -820,6 +783,55 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(Params p) {
         acc[2 * e] += w * __uint_as_float(raw[u][e] << 16);
         acc[2 * e + 1] += w * __uint_as_float(raw[u][e] & 0xFFFF0000u);
       }
+    }
+  };
+  bool live;
+  if constexpr (kSpec) {
+    // the launch gives kBatch >= every split count of the plan: one batch
+    float2 ml[kBatch];
+    u32x4 raw[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int su = u < ns_plan ? u : (ns_plan > 0 ? ns_plan - 1 : 0);
+      ml[u] = p.part_ml[ro + su];
+      raw[u] = *reinterpret_cast<const u32x4*>(p.part_o + (ro + su) * D + lane * 8);
+    }
+    // every load above is issued before the first use of the sizes waits
+    __builtin_amdgcn_sched_barrier(0);
+    const int nq = min(nq_r, p.n_q_max);
+    const int T = prefix_r + nq;
+    live = qi < nq && T > 0;
+    const int ntiles = (T + kKT - 1) / kKT;
+    const int ns = live ? request_splits(ns_plan, ntiles, p) : 0;
+    // slots past the request's splits (repeats included) or left empty
+    if (ns < kBatch || ntiles < ns) {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (!(u < ns && split_nonempty(u, ns, ntiles, p))) {
+          ml[u] = make_float2(-INFINITY, 0.f);
+          raw[u] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+    if (live) merge(ml, raw);
+  } else {
+    const int nq = min(nq_r, p.n_q_max);
+    const int T = prefix_r + nq;
+    live = qi < nq && T > 0;
+    const int ntiles = (T + kKT - 1) / kKT;
+    const int ns = live ? request_splits(ns_plan, ntiles, p) : 0;
+    for (int sp0 = 0; sp0 < ns; sp0 += kBatch) {
+      float2 ml[kBatch];
+      u32x4 raw[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int sp = sp0 + u;
+        const bool ok = sp < ns && split_nonempty(sp, ns, ntiles, p);
+        ml[u] = ok ? p.part_ml[ro + sp] : make_float2(-INFINITY, 0.f);
+        raw[u] = ok ? *reinterpret_cast<const u32x4*>(p.part_o + (ro + sp) * D + lane * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
+      }
+      merge(ml, raw);
     }
   }
   if (!live) return;
@@ -855,9 +867,9 @@ hipError_t launch_d(const Params& prm, const AttnPlan& plan, hipStream_t stream)
     const int threads = (long)rows * (D / 8) < 256L * kCUs ? 64 : 256;
     const int rpb = threads / (D / 8);
     // 8 slots per batch when the plan has at most 8 splits (fewer repeated
-    // or empty slots), else 16
+    // or empty slots), else 16; a single request's plan in one batch
     const dim3 grid((rows + rpb - 1) / rpb);
-    if (prm.batch == 1) {
+    if (prm.batch == 1 && max_split <= 16) {
       if (max_split <= 8)
         hipLaunchKernelGGL((attn_combine_kernel<D, 8, true>), grid, dim3(threads), 0, stream,
                            prm);
